@@ -1,0 +1,283 @@
+/*
+ * attn_oracle.c -- plain fp64 CPU oracle for causal RoPE attention forward.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file: only the tests, the smoke check and the benchmark's CPU
+ * baseline leg use it.  It shares no code, header, table or constant with
+ * the HIP library in attention_attn_fwd_04_amd/csrc.
+ *
+ * What it computes (each step cites the page that defines it):
+ *
+ *  1. bf16 inputs are widened to fp64 exactly (a bf16 value is the top half
+ *     of an IEEE binary32 word).
+ *  2. RoPE, NeoX convention ("AttnFuse: A Composable DSL for Compiling
+ *     Attentions to Fused GPU Kernels", section 2 "Rotary Position
+ *     Embeddings" and section 4.1 "Fused RoPE"): dimension pair r is
+ *     (r, r + D/2); at position p it is rotated by the angle
+ *     p * theta^(-2r/D):
+ *        x'[r]       = x[r] cos - x[r+D/2] sin
+ *        x'[r+D/2]   = x[r+D/2] cos + x[r] sin
+ *     theta == 0 means "no rotation".
+ *  3. Scores ("Attention block decomposition", "Three shapes, two
+ *     reductions"): s(n,m) = scale * sum over pairs of the pair terms
+ *     q'[r]k'[r] + q'[r+D/2]k'[r+D/2], contracted over D.
+ *  4. Optional per-pair distance window ("ATFlash -- Per-RoPE-Wavelength
+ *     Attention Windows", "The idea"): pair r contributes to s(n,m) only when
+ *     n - m <= w[r].  The table is w[r] = floor(k * lambda_r) with the pair's
+ *     wavelength lambda_r = 2*pi*theta^(2r/D).
+ *  5. Causal mask: keys m > n are excluded ("Flash Attention: Causal Prefill
+ *     D=128", "Reverse traversal isolates the causal mask").
+ *  6. Row softmax over the materialised score row, then O = P V, contracted
+ *     over the key axis ("Attention block decomposition").  No intermediate
+ *     rounding: everything stays fp64.  The online-softmax recurrence the
+ *     kernels use is exact ("AttnFuse", section 2 "FlashAttention and online
+ *     softmax"), so the plain definition is the reference.
+ *  7. Grouped-query attention: query head hq reads KV head hq / (Hq/Hkv).
+ *
+ * Layout of every tensor: [B, S, H, D] contiguous ("BSHD"), bf16 bits as
+ * uint16_t.  Positions are 0..S-1 plus an optional common offset, which the
+ * invariance tests use (scores depend only on n - m).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+static double widen_bf16(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* Step 2 for one row: x (D values, fp64) at position pos -> out. */
+static void rotate_row(const double *x, int D, double theta, double pos,
+                       double *out)
+{
+    int half = D / 2;
+    if (theta == 0.0) {
+        memcpy(out, x, sizeof(double) * (size_t)D);
+        return;
+    }
+    for (int r = 0; r < half; ++r) {
+        double freq = pow(theta, -2.0 * (double)r / (double)D);
+        double ang = pos * freq;
+        double c = cos(ang), s = sin(ang);
+        out[r] = x[r] * c - x[r + half] * s;
+        out[r + half] = x[r + half] * c + x[r] * s;
+    }
+}
+
+/* Exported: rotate one bf16 row (used by the convention tests). */
+void oracle_rope_row(const uint16_t *x, int D, double theta, double pos,
+                     double *out)
+{
+    double tmp[1024];
+    for (int d = 0; d < D; ++d)
+        tmp[d] = widen_bf16(x[d]);
+    rotate_row(tmp, D, theta, pos, out);
+}
+
+/* Step 3 + 4 for one (query, key) pair of rotated rows. */
+static double score(const double *qr, const double *kr, int D, double scale,
+                    const int32_t *window, long long dist)
+{
+    int half = D / 2;
+    double acc = 0.0;
+    for (int r = 0; r < half; ++r) {
+        if (window != NULL && dist > (long long)window[r])
+            continue;
+        acc += qr[r] * kr[r] + qr[r + half] * kr[r + half];
+    }
+    return scale * acc;
+}
+
+static const uint16_t *row_ptr(const uint16_t *t, int S, int H, int D, int b,
+                               int s, int h)
+{
+    return t + (((size_t)b * S + s) * H + h) * (size_t)D;
+}
+
+/* Rotated K for every position of one (b, hk) head: S x D fp64. */
+static double *rotated_keys(const uint16_t *k, int S, int Hkv, int D, int b,
+                            int hk, double theta, long long pos_offset)
+{
+    double *kr = (double *)malloc(sizeof(double) * (size_t)S * D);
+    if (!kr)
+        return NULL;
+#pragma omp parallel for schedule(static)
+    for (int m = 0; m < S; ++m) {
+        double raw[1024];
+        const uint16_t *src = row_ptr(k, S, Hkv, D, b, m, hk);
+        for (int d = 0; d < D; ++d)
+            raw[d] = widen_bf16(src[d]);
+        rotate_row(raw, D, theta, (double)(m + pos_offset), kr + (size_t)m * D);
+    }
+    return kr;
+}
+
+/*
+ * Attention output for a list of query rows.
+ *   rows: n_rows triples (b, n, hq)
+ *   out:  n_rows x D fp64
+ *   lse:  optional n_rows natural-log log-sum-exp of the row's scores
+ * Returns 0, or -1 on bad arguments / allocation failure.
+ */
+int oracle_attn_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                     int B, int S, int Hq, int Hkv, int D, double rope_theta,
+                     int causal, double scale, const int32_t *window,
+                     long long pos_offset, const int32_t *rows,
+                     long long n_rows, double *out, double *lse)
+{
+    if (B < 0 || S < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || D > 1024 ||
+        (D % 2) != 0 || (Hq % Hkv) != 0)
+        return -1;
+    int group = Hq / Hkv;
+    for (long long i = 0; i < n_rows; ++i) {
+        int b = rows[3 * i], n = rows[3 * i + 1], hq = rows[3 * i + 2];
+        if (b < 0 || b >= B || n < 0 || n >= S || hq < 0 || hq >= Hq)
+            return -1;
+    }
+    int status = 0;
+    for (int b = 0; b < B && status == 0; ++b) {
+        for (int hk = 0; hk < Hkv && status == 0; ++hk) {
+            /* Does any requested row read this KV head? */
+            long long any = 0;
+            for (long long i = 0; i < n_rows; ++i)
+                if (rows[3 * i] == b && rows[3 * i + 2] / group == hk)
+                    ++any;
+            if (!any)
+                continue;
+            double *kr = rotated_keys(k, S, Hkv, D, b, hk, rope_theta, pos_offset);
+            if (!kr) {
+                status = -1;
+                break;
+            }
+#pragma omp parallel for schedule(dynamic, 1)
+            for (long long i = 0; i < n_rows; ++i) {
+                if (rows[3 * i] != b || rows[3 * i + 2] / group != hk)
+                    continue;
+                int n = rows[3 * i + 1], hq = rows[3 * i + 2];
+                double qraw[1024], qr[1024];
+                const uint16_t *qs = row_ptr(q, S, Hq, D, b, n, hq);
+                for (int d = 0; d < D; ++d)
+                    qraw[d] = widen_bf16(qs[d]);
+                rotate_row(qraw, D, rope_theta, (double)(n + pos_offset), qr);
+
+                int m_end = causal ? n + 1 : S; /* keys 0..m_end-1 */
+                double *srow = (double *)malloc(sizeof(double) * (size_t)(m_end > 0 ? m_end : 1));
+                double mu = -INFINITY;
+                for (int m = 0; m < m_end; ++m) {
+                    srow[m] = score(qr, kr + (size_t)m * D, D, scale, window,
+                                    (long long)n - (long long)m);
+                    if (srow[m] > mu)
+                        mu = srow[m];
+                }
+                double z = 0.0;
+                for (int m = 0; m < m_end; ++m) {
+                    srow[m] = exp(srow[m] - mu);
+                    z += srow[m];
+                }
+                double *o = out + (size_t)i * D;
+                for (int d = 0; d < D; ++d)
+                    o[d] = 0.0;
+                for (int m = 0; m < m_end; ++m) {
+                    double p = srow[m] / z;
+                    const uint16_t *vs = row_ptr(v, S, Hkv, D, b, m, hk);
+                    for (int d = 0; d < D; ++d)
+                        o[d] += p * widen_bf16(vs[d]);
+                }
+                if (lse)
+                    lse[i] = mu + log(z);
+                free(srow);
+            }
+            free(kr);
+        }
+    }
+    return status;
+}
+
+/*
+ * The scaled score row s(n, m) for m = 0..S-1 of one query (b, n, hq), with
+ * masked keys (m > n under the causal mask) set to -inf.  Used by the
+ * invariance and window tests.
+ */
+int oracle_scores_row(const uint16_t *q, const uint16_t *k, int B, int S,
+                      int Hq, int Hkv, int D, double rope_theta, int causal,
+                      double scale, const int32_t *window, long long pos_offset,
+                      int b, int n, int hq, double *scores)
+{
+    if (b < 0 || b >= B || n < 0 || n >= S || hq < 0 || hq >= Hq ||
+        D <= 0 || D > 1024 || (Hq % Hkv) != 0)
+        return -1;
+    int hk = hq / (Hq / Hkv);
+    double raw[1024], qr[1024], kr[1024];
+    const uint16_t *qs = row_ptr(q, S, Hq, D, b, n, hq);
+    for (int d = 0; d < D; ++d)
+        raw[d] = widen_bf16(qs[d]);
+    rotate_row(raw, D, rope_theta, (double)(n + pos_offset), qr);
+    for (int m = 0; m < S; ++m) {
+        if (causal && m > n) {
+            scores[m] = -INFINITY;
+            continue;
+        }
+        const uint16_t *ks = row_ptr(k, S, Hkv, D, b, m, hk);
+        for (int d = 0; d < D; ++d)
+            raw[d] = widen_bf16(ks[d]);
+        rotate_row(raw, D, rope_theta, (double)(m + pos_offset), kr);
+        scores[m] = score(qr, kr, D, scale, window, (long long)n - (long long)m);
+    }
+    return 0;
+}
+
+/*
+ * Window table ("ATFlash", "The idea"): w[r] = floor(k_turns * lambda_r),
+ * lambda_r = 2*pi*theta^(2r/D), for r = 0..D/2-1, evaluated in fp64.
+ */
+int oracle_window_table(double rope_theta, int D, double k_turns, int32_t *w)
+{
+    if (D <= 0 || (D % 2) != 0 || !(rope_theta > 1.0) || !(k_turns > 0.0))
+        return -1;
+    const double two_pi = 6.283185307179586476925286766559;
+    for (int r = 0; r < D / 2; ++r) {
+        double lam = two_pi * pow(rope_theta, 2.0 * (double)r / (double)D);
+        double wr = floor(k_turns * lam);
+        w[r] = wr > 2147483647.0 ? 2147483647 : (int32_t)wr;
+    }
+    return 0;
+}
+
+/*
+ * Pair terms removed by the window over one head's causal triangle
+ * (0 <= m <= n < S): for each pair r, the cells with distance
+ * delta = n - m > w[r].  Distance delta occurs S - delta times, so pair r
+ * removes sum_{delta = max(w[r]+1, 0)}^{S-1} (S - delta) cells, which is the
+ * triangular number T(S - lo) with lo = max(w[r]+1, 0).
+ */
+long long oracle_pruned_terms(const int32_t *w, int D, int S)
+{
+    long long total = 0;
+    for (int r = 0; r < D / 2; ++r) {
+        long long lo = (long long)w[r] + 1;
+        if (lo < 0)
+            lo = 0;
+        if (lo > S - 1)
+            continue;
+        long long cnt = (long long)S - lo; /* number of distances lo..S-1 */
+        total += cnt * (cnt + 1) / 2;
+    }
+    return total;
+}

@@ -1,0 +1,323 @@
+"""Pins of the fp64 oracle against things other than itself (CPU only).
+
+Each test checks the oracle against a library routine, a closed form, an
+invariant the pages state, or an independent brute force, chosen so that a
+plausible slip (wrong pairing, wrong rotation sign, dropped scale, wrong GQA
+index, off-by-one causal mask, wrong window comparison) fails at least one.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from attention_attn_fwd_04_amd.inputs import bf16_bits, make_qkv
+from oracle import brute
+from oracle import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _qkv_np(B, S, Hq, Hkv, D, seed, dist="normal"):
+    q, k, v = make_qkv(B, S, Hq, Hkv, D, seed, dist)
+    return bf16_bits(q), bf16_bits(k), bf16_bits(v)
+
+
+def _f64(a):
+    return O.bf16_bits_to_f64(a)
+
+
+# --------------------------------------------------------------------------
+# RoPE convention: NeoX pairing (r, r + D/2), rotation direction, frequencies.
+# Pinned to the Hugging Face transformers implementation (rotate_half form).
+# --------------------------------------------------------------------------
+def _hf_rotate(x64, theta, pos, inv_freq=None):
+    from transformers.models.llama.modeling_llama import apply_rotary_pos_emb
+    D = x64.shape[-1]
+    if inv_freq is None:
+        inv_freq = 1.0 / (theta ** (torch.arange(0, D, 2, dtype=torch.float64) / D))
+    freqs = torch.tensor([float(pos)], dtype=torch.float64)[:, None] * inv_freq[None, :]
+    emb = torch.cat([freqs, freqs], dim=-1)
+    cos, sin = emb.cos()[None], emb.sin()[None]            # [1, 1, D]
+    t = torch.from_numpy(x64)[None, None, None, :]          # [1, 1(head), 1(seq), D]
+    qr, _ = apply_rotary_pos_emb(t, t, cos, sin, unsqueeze_dim=1)
+    return qr.reshape(-1).numpy()
+
+
+@pytest.mark.parametrize("D,theta", [(64, 1e4), (128, 1e4), (128, 5e5)])
+@pytest.mark.parametrize("pos", [0, 1, 17, 4095, 32767])
+def test_rope_matches_transformers(D, theta, pos):
+    q, _, _ = _qkv_np(1, 1, 1, 1, D, seed=pos + D)
+    x = q.reshape(-1)
+    ours = O.rope_row(x, theta, pos)
+    ref = _hf_rotate(_f64(x), theta, pos)
+    np.testing.assert_allclose(ours, ref, rtol=0, atol=1e-12 * max(1.0, pos))
+
+
+def test_rope_frequency_formula_matches_llama_rotary_embedding():
+    """LlamaRotaryEmbedding builds its own inverse frequencies (fp32)."""
+    from transformers import LlamaConfig
+    from transformers.models.llama.modeling_llama import LlamaRotaryEmbedding
+    D, theta = 128, 1e4
+    cfg = LlamaConfig(hidden_size=D * 2, num_attention_heads=2, head_dim=D,
+                      rope_theta=theta, max_position_embeddings=4096)
+    emb = LlamaRotaryEmbedding(cfg)
+    x = torch.zeros(1, 1, 8, D, dtype=torch.float64)
+    cos, sin = emb(x, torch.arange(8)[None])
+    q, _, _ = _qkv_np(1, 1, 1, 1, D, seed=5)
+    xrow = q.reshape(-1)
+    for p in range(8):
+        from transformers.models.llama.modeling_llama import apply_rotary_pos_emb
+        t = torch.from_numpy(_f64(xrow))[None, None, None, :]
+        ref, _ = apply_rotary_pos_emb(t, t, cos[:, p:p + 1], sin[:, p:p + 1], unsqueeze_dim=1)
+        np.testing.assert_allclose(O.rope_row(xrow, theta, p), ref.reshape(-1).numpy(),
+                                   rtol=0, atol=2e-5)
+
+
+def test_rope_worked_example_closed_form():
+    """D=4, theta=100: pair 0 turns by p rad, pair 1 by p/10 rad."""
+    x = np.array([1.0, 2.0, 3.0, 4.0], dtype=np.float32)
+    bits = (x.view(np.uint32) >> 16).astype(np.uint16)
+    for p in (1.0, 2.0, 7.0):
+        a0, a1 = p, p / 10.0
+        exp = [1 * math.cos(a0) - 3 * math.sin(a0), 2 * math.cos(a1) - 4 * math.sin(a1),
+               3 * math.cos(a0) + 1 * math.sin(a0), 4 * math.cos(a1) + 2 * math.sin(a1)]
+        np.testing.assert_allclose(O.rope_row(bits, 100.0, p), exp, rtol=0, atol=1e-14)
+
+
+def test_rope_theta_zero_is_identity():
+    q, _, _ = _qkv_np(1, 1, 1, 1, 128, seed=9)
+    np.testing.assert_array_equal(O.rope_row(q.reshape(-1), 0.0, 1234), _f64(q.reshape(-1)))
+
+
+def test_rope_preserves_pair_norms():
+    q, _, _ = _qkv_np(1, 1, 1, 1, 128, seed=11)
+    x = _f64(q.reshape(-1))
+    y = O.rope_row(q.reshape(-1), 1e4, 777)
+    h = 64
+    np.testing.assert_allclose(y[:h] ** 2 + y[h:] ** 2, x[:h] ** 2 + x[h:] ** 2, rtol=1e-13, atol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# Scores: relative-angle identity and shift invariance (AttnFuse section 2;
+# ATFlash "The idea": each pair contributes through the angle (n - m) theta_r).
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("theta", [1e4, 5e5])
+def test_scores_relative_angle_identity(theta):
+    B, S, H, D = 1, 40, 1, 64
+    q, k, _ = _qkv_np(B, S, H, H, D, seed=3)
+    scale = 1 / math.sqrt(D)
+    qf, kf = _f64(q)[0, :, 0], _f64(k)[0, :, 0]
+    h = D // 2
+    r = np.arange(h)
+    inv = theta ** (-2.0 * r / D)
+    for n in (0, 5, 39):
+        s = O.scores_row(q, k, 0, n, 0, theta, True, scale)
+        for m in range(S):
+            if m > n:
+                assert s[m] == -np.inf
+                continue
+            phi = (m - n) * inv
+            q1, q2, k1, k2 = qf[n, :h], qf[n, h:], kf[m, :h], kf[m, h:]
+            ref = scale * np.sum(np.cos(phi) * (q1 * k1 + q2 * k2) + np.sin(phi) * (q2 * k1 - q1 * k2))
+            assert abs(s[m] - ref) < 1e-12 * max(1.0, abs(ref))
+
+
+def test_output_shift_invariant():
+    B, S, Hq, Hkv, D = 1, 48, 2, 1, 64
+    q, k, v = _qkv_np(B, S, Hq, Hkv, D, seed=4)
+    a = O.attn_full(q, k, v, 1e4, True, 1 / math.sqrt(D), pos_offset=0)
+    b = O.attn_full(q, k, v, 1e4, True, 1 / math.sqrt(D), pos_offset=1000)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-10)
+
+
+# --------------------------------------------------------------------------
+# Attention core: torch's fp64 scaled_dot_product_attention on inputs rotated
+# by the transformers routine (library special case).
+# --------------------------------------------------------------------------
+def _sdpa_reference(q, k, v, theta, causal, scale):
+    from transformers.models.llama.modeling_llama import apply_rotary_pos_emb
+    B, S, Hq, D = q.shape
+    qt = torch.from_numpy(_f64(q)).permute(0, 2, 1, 3)  # B H S D
+    kt = torch.from_numpy(_f64(k)).permute(0, 2, 1, 3)
+    vt = torch.from_numpy(_f64(v)).permute(0, 2, 1, 3)
+    if theta:
+        inv = 1.0 / (theta ** (torch.arange(0, D, 2, dtype=torch.float64) / D))
+        fr = torch.arange(S, dtype=torch.float64)[:, None] * inv[None, :]
+        emb = torch.cat([fr, fr], -1)
+        qt, kt = apply_rotary_pos_emb(qt, kt, emb.cos()[None], emb.sin()[None], unsqueeze_dim=1)
+    o = torch.nn.functional.scaled_dot_product_attention(
+        qt.contiguous(), kt.contiguous(), vt.contiguous(), is_causal=bool(causal),
+        scale=scale, enable_gqa=(Hq != k.shape[2]))
+    return o.permute(0, 2, 1, 3).numpy()
+
+
+@pytest.mark.parametrize("B,S,Hq,Hkv,D,theta,causal", [
+    (1, 64, 2, 2, 64, 1e4, True),
+    (2, 37, 4, 2, 64, 1e4, True),
+    (1, 50, 4, 1, 128, 5e5, True),
+    (1, 33, 2, 2, 64, 1e4, False),
+    (1, 40, 2, 2, 64, 0.0, True),
+])
+def test_matches_torch_sdpa_fp64(B, S, Hq, Hkv, D, theta, causal):
+    q, k, v = _qkv_np(B, S, Hq, Hkv, D, seed=S + D)
+    scale = 1 / math.sqrt(D)
+    ours = O.attn_full(q, k, v, theta, causal, scale)
+    ref = _sdpa_reference(q, k, v, theta, causal, scale)
+    np.testing.assert_allclose(ours, ref, rtol=0, atol=1e-12)
+
+
+def test_scale_is_applied_once():
+    """Doubling scale must equal doubling Q (both scale every score by 2)."""
+    B, S, H, D = 1, 24, 1, 64
+    q, k, v = _qkv_np(B, S, H, H, D, seed=12)
+    q2 = (_f64(q) * 2).astype(np.float32).view(np.uint32) >> 16
+    q2 = q2.astype(np.uint16)  # exact: doubling a bf16 value is exact
+    a = O.attn_full(q, k, v, 1e4, True, 2 / math.sqrt(D))
+    b = O.attn_full(q2, k, v, 1e4, True, 1 / math.sqrt(D))
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# Closed forms of the causal mask.
+# --------------------------------------------------------------------------
+def test_causal_row0_equals_v0_exactly():
+    q, k, v = _qkv_np(2, 32, 4, 2, 64, seed=7)
+    out = O.attn_full(q, k, v, 1e4, True, 0.125)
+    for b in range(2):
+        for h in range(4):
+            np.testing.assert_array_equal(out[b, 0, h], _f64(v)[b, 0, h // 2])
+
+
+def test_zero_queries_give_prefix_means():
+    B, S, H, D = 1, 30, 2, 64
+    _, k, v = _qkv_np(B, S, H, H, D, seed=8)
+    q = np.zeros((B, S, H, D), dtype=np.uint16)
+    out = O.attn_full(q, k, v, 1e4, True, 0.125)
+    vf = _f64(v)
+    ref = np.cumsum(vf, axis=1) / np.arange(1, S + 1)[None, :, None, None]
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-13)
+    out_nc = O.attn_full(q, k, v, 1e4, False, 0.125)
+    np.testing.assert_allclose(out_nc, np.broadcast_to(vf.mean(axis=1, keepdims=True), out.shape),
+                               rtol=0, atol=1e-13)
+
+
+def test_constant_v_gives_constant_output():
+    B, S, H, D = 1, 40, 2, 64
+    q, k, _ = _qkv_np(B, S, H, H, D, seed=10)
+    row = _qkv_np(1, 1, 1, 1, D, seed=99)[2].reshape(-1)
+    v = np.broadcast_to(row, (B, S, H, D)).copy()
+    out = O.attn_full(q, k, v, 1e4, True, 0.125)
+    np.testing.assert_allclose(out, np.broadcast_to(_f64(row), out.shape), rtol=0, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# Independent brute force (per-pair materialisation, explicit 2x2 matrices).
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("use_window", [False, True])
+def test_matches_brute_force(causal, use_window):
+    B, S, Hq, Hkv, D = 2, 13, 4, 2, 8
+    q, k, v = _qkv_np(B, S, Hq, Hkv, D, seed=21)
+    window = np.array([0, 2, 5, 11], dtype=np.int32) if use_window else None
+    if use_window and not causal:
+        pytest.skip("the window is defined on the causal triangle")
+    scale = 0.35
+    ours = O.attn_full(q, k, v, 50.0, causal, scale, window)
+    ref = brute.attention(_f64(q), _f64(k), _f64(v), 50.0, causal, scale, window)
+    np.testing.assert_allclose(ours, ref, rtol=0, atol=1e-13)
+
+
+def test_window_scores_match_brute_force():
+    B, S, H, D = 1, 20, 1, 16
+    q, k, _ = _qkv_np(B, S, H, H, D, seed=22)
+    window = np.array([1, 1, 3, 4, 7, 9, 15, 30], dtype=np.int32)
+    _, sc = brute.attention_head(_f64(q)[0, :, 0], _f64(k)[0, :, 0], _f64(k)[0, :, 0],
+                                 1e4, True, 0.25, window)
+    for n in range(S):
+        s = O.scores_row(q, k, 0, n, 0, 1e4, True, 0.25, window)
+        np.testing.assert_allclose(s, sc[n], rtol=0, atol=1e-13)
+
+
+def test_window_all_kept_is_bitwise_no_window():
+    B, S, Hq, Hkv, D = 1, 64, 2, 2, 64
+    q, k, v = _qkv_np(B, S, Hq, Hkv, D, seed=23)
+    big = np.full(D // 2, S - 1, dtype=np.int32)
+    a = O.attn_full(q, k, v, 1e4, True, 0.125, None)
+    b = O.attn_full(q, k, v, 1e4, True, 0.125, big)
+    np.testing.assert_array_equal(a, b)
+
+
+def test_window_zero_keeps_only_the_diagonal_term():
+    """All w_r = -1 removes every pair at every distance >= 0: all scores are
+    zero, so each causal row is the prefix mean of V."""
+    B, S, H, D = 1, 16, 1, 16
+    q, k, v = _qkv_np(B, S, H, H, D, seed=24)
+    w = np.full(D // 2, -1, dtype=np.int32)
+    out = O.attn_full(q, k, v, 1e4, True, 0.25, w)
+    vf = _f64(v)
+    ref = np.cumsum(vf, axis=1) / np.arange(1, S + 1)[None, :, None, None]
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# Window table and pruned-term counts.
+# --------------------------------------------------------------------------
+def _mp_table(theta, D, k):
+    import mpmath
+    mpmath.mp.dps = 60
+    out, gap = [], 1.0
+    for r in range(D // 2):
+        val = mpmath.mpf(k) * 2 * mpmath.pi * mpmath.power(mpmath.mpf(theta), mpmath.mpf(2 * r) / D)
+        fl = int(mpmath.floor(val))
+        out.append(fl)
+        gap = min(gap, float(val - fl), float(fl + 1 - val))
+    return np.array(out, dtype=np.int64), gap
+
+
+@pytest.mark.parametrize("theta,D,k", [(5e5, 128, 2.0), (1e4, 64, 2.0), (1e4, 128, 2.0), (5e5, 128, 1.0)])
+def test_window_table_matches_high_precision(theta, D, k):
+    ref, gap = _mp_table(theta, D, k)
+    ours = O.window_table(theta, D, k)
+    assert gap > 1e-6  # no value sits near an integer, so fp64 floor is safe
+    clipped = np.minimum(ref, 2**31 - 1)
+    np.testing.assert_array_equal(ours.astype(np.int64), clipped)
+    assert np.all(np.diff(ours) >= 0)
+
+
+@pytest.mark.parametrize("S", [1, 2, 13, 64, 100])
+def test_pruned_terms_closed_form_matches_counting(S):
+    rng = np.random.default_rng(S)
+    for trial in range(4):
+        w = np.sort(rng.integers(-2, S + 3, size=8)).astype(np.int32)
+        assert O.pruned_terms(w, 16, S) == brute.pruned_terms_count(w, S)
+    w = O.window_table(1e4, 16, 2.0)
+    assert O.pruned_terms(w, 16, S) == brute.pruned_terms_count(w, S)
+
+
+def test_pruned_share_grows_logarithmically():
+    """ATFlash ("The idea"): the pruned share is input independent and grows
+    with N.  For theta=5e5, D=128, k=2 it rises monotonically with S."""
+    w = O.window_table(5e5, 128, 2.0)
+    shares = []
+    for S in (256, 4096, 8192, 16384, 32768):
+        total = 64 * S * (S + 1) // 2
+        shares.append(O.pruned_terms(w, 128, S) / total)
+    assert all(a < b for a, b in zip(shares, shares[1:]))
+    assert 0.45 < shares[-1] < 0.55
+
+
+# --------------------------------------------------------------------------
+# Constants the pages print.
+# --------------------------------------------------------------------------
+def test_printed_softmax_constant_and_flop_formula():
+    with open(os.path.join(GOLDEN, "croqtile_causal_prefill_d128.json")) as f:
+        g = json.load(f)
+    c = math.log2(math.e) / math.sqrt(128)
+    assert round(c, g["printed_digits"]) == g["log2e_over_sqrt_d128_printed"]
+    w = g["workload"]
+    for row in g["fa3_rows"]:
+        flops = 2 * w["B"] * w["H"] * row["S"] ** 2 * w["D"]
+        assert abs(flops / (row["ms"] * 1e9) - row["tflops"]) < 0.05
