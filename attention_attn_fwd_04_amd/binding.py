@@ -1,0 +1,171 @@
+"""Thin ctypes binding over libattn_mi355x.so (the C ABI in include/attn.h).
+
+Argument marshalling only: torch tensors supply device pointers and the
+current HIP stream; every step of the computation runs in the library's HIP
+kernels.  There is no fallback: if the library is missing or no gfx950
+device is current, the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libattn_mi355x.so")
+
+ATTN_OK = 0
+ATTN_EINVAL = -1
+ATTN_EUNSUPPORTED = -2
+ATTN_EALIGN = -3
+ATTN_ENOMEM = -4
+ATTN_ELAUNCH = -5
+ATTN_ENODEVICE = -6
+
+EXPORTED = ("attn_fwd", "attn_rope_apply", "attn_window_table", "attn_pruned_terms",
+            "attn_check_args", "attn_strerror", "attn_release")
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__("%s failed: %s (status %d)" % (what, strerror(status), status))
+
+
+def lib():
+    """Load the built library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("HIP library %s is not built; run `python -m "
+                           "attention_attn_fwd_04_amd.build`" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i, f, d = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_double
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    L.attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, f, i, f, i32p, vp]
+    L.attn_fwd.restype = i
+    L.attn_rope_apply.argtypes = [vp, vp, vp, vp, i, i, i, i, i, f, vp]
+    L.attn_rope_apply.restype = i
+    L.attn_window_table.argtypes = [d, i, d, i32p]
+    L.attn_window_table.restype = i
+    L.attn_pruned_terms.argtypes = [i32p, i, i, ctypes.POINTER(ctypes.c_longlong)]
+    L.attn_pruned_terms.restype = i
+    L.attn_check_args.argtypes = [vp, vp, vp, vp, i, i, i, i, i, f, i, f, i32p]
+    L.attn_check_args.restype = i
+    L.attn_strerror.argtypes = [i]
+    L.attn_strerror.restype = ctypes.c_char_p
+    L.attn_release.argtypes = []
+    L.attn_release.restype = None
+    _lib = L
+    return L
+
+
+def strerror(status: int) -> str:
+    return lib().attn_strerror(int(status)).decode()
+
+
+def _window_ptr(window_table, D):
+    if window_table is None:
+        return None, None
+    w = np.ascontiguousarray(np.asarray(window_table, dtype=np.int32))
+    if w.shape != (D // 2,):
+        raise ValueError("window_table must hold D/2 = %d int32 values" % (D // 2))
+    return w, w.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def _stream_handle(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check_tensor(t, name):
+    import torch
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or t.dim() != 4:
+        raise TypeError("%s must be a 4-d bfloat16 tensor [B, S, H, D]" % name)
+    if not t.is_cuda:
+        raise TypeError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous (BSHD)" % name)
+
+
+def attn_fwd(q, k, v, o=None, *, rope_theta=10000.0, causal=True, scale=None,
+             window_table=None, stream=None):
+    """Fused causal attention forward with RoPE at load; returns o [B,S,Hq,D]."""
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check_tensor(t, n)
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if k.shape != (B, S, Hkv, D) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, S, Hkv, D] matching q")
+    if o is None:
+        o = torch.empty_like(q)
+    else:
+        _check_tensor(o, "o")
+        if o.shape != q.shape:
+            raise ValueError("o must have q's shape")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    w, wp = _window_ptr(window_table, D)
+    st = lib().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), B, Hq, Hkv, S, D,
+                        float(rope_theta), int(bool(causal)), float(scale), wp, _stream_handle(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd")
+    return o
+
+
+def attn_rope_apply(q, k, q_out=None, k_out=None, *, rope_theta=10000.0, stream=None):
+    """Separate RoPE pass: rotated copies (q_out, k_out) of q and k."""
+    import torch
+    _check_tensor(q, "q")
+    _check_tensor(k, "k")
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if k.shape != (B, S, Hkv, D):
+        raise ValueError("k must be [B, S, Hkv, D] matching q")
+    q_out = torch.empty_like(q) if q_out is None else q_out
+    k_out = torch.empty_like(k) if k_out is None else k_out
+    _check_tensor(q_out, "q_out")
+    _check_tensor(k_out, "k_out")
+    st = lib().attn_rope_apply(q.data_ptr(), k.data_ptr(), q_out.data_ptr(), k_out.data_ptr(),
+                               B, Hq, Hkv, S, D, float(rope_theta), _stream_handle(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_rope_apply")
+    return q_out, k_out
+
+
+def attn_window_table(rope_theta, D, k_turns=2.0):
+    out = np.zeros(D // 2, dtype=np.int32)
+    st = lib().attn_window_table(float(rope_theta), int(D), float(k_turns),
+                                 out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_window_table")
+    return out
+
+
+def attn_pruned_terms(window_table, D, S) -> int:
+    w, wp = _window_ptr(window_table, D)
+    res = ctypes.c_longlong(0)
+    st = lib().attn_pruned_terms(wp, int(D), int(S), ctypes.byref(res))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_pruned_terms")
+    return int(res.value)
+
+
+def attn_check_args(q_ptr, k_ptr, v_ptr, o_ptr, B, Hq, Hkv, S, D, rope_theta, causal, scale,
+                    window_table=None) -> int:
+    """Raw host-side validation on integer addresses; returns the status."""
+    w, wp = _window_ptr(window_table, D) if window_table is not None else (None, None)
+    return int(lib().attn_check_args(q_ptr, k_ptr, v_ptr, o_ptr, B, Hq, Hkv, S, D,
+                                     float(rope_theta), int(causal), float(scale), wp))
+
+
+def attn_release():
+    lib().attn_release()

@@ -1,0 +1,279 @@
+// attn_api.cpp -- host side of the C ABI declared in include/attn.h:
+// argument validation, the per-device RoPE cos/sin table cache, dispatch to
+// the gfx950 kernels, and the host-only window helpers.
+#include "../../include/attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "attn_internal.h"
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb)
+{
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+int check_shapes(int B, int Hq, int Hkv, int S, int D)
+{
+    if (B < 0 || S < 0 || Hq < 1 || Hkv < 1) return ATTN_EINVAL;
+    if (Hq % Hkv != 0) return ATTN_EINVAL;
+    if (D != 64 && D != 128) return (D > 0 && D % 2 == 0) ? ATTN_EUNSUPPORTED : ATTN_EINVAL;
+    // Element offsets must fit the kernels' 32-bit block indexing and size_t.
+    const long long rows = (long long)B * S * (long long)(Hq > Hkv ? Hq : Hkv);
+    if (rows > (1LL << 40)) return ATTN_EINVAL;
+    const long long q_tiles = ((long long)S + 255) / 256;
+    if (q_tiles * Hq * (long long)B > 0x7fffffffLL) return ATTN_EINVAL;
+    return ATTN_OK;
+}
+
+int check_theta(float rope_theta)
+{
+    if (rope_theta == 0.0f) return ATTN_OK;
+    if (!std::isfinite(rope_theta) || !(rope_theta > 1.0f)) return ATTN_EINVAL;
+    return ATTN_OK;
+}
+
+// ---- device check ---------------------------------------------------------
+std::mutex g_mu;
+std::map<int, bool> g_dev_ok;
+
+int current_device_ok(int *dev_out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return ATTN_ENODEVICE;
+    *dev_out = dev;
+    std::lock_guard<std::mutex> lk(g_mu);
+    auto it = g_dev_ok.find(dev);
+    if (it == g_dev_ok.end()) {
+        hipDeviceProp_t prop;
+        bool ok = false;
+        if (hipGetDeviceProperties(&prop, dev) == hipSuccess)
+            ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+        it = g_dev_ok.emplace(dev, ok).first;
+    }
+    return it->second ? ATTN_OK : ATTN_ENODEVICE;
+}
+
+// ---- RoPE cos/sin tables ---------------------------------------------------
+// Built in fp64 on the host and stored as fp32 (layout documented on
+// attn::RopeTable).  One table per (device, D, theta), grown on demand;
+// replaced tables are kept until attn_release because work already enqueued
+// may still read them.
+struct TableKey {
+    int dev, D;
+    uint32_t theta_bits;
+    bool operator<(const TableKey &o) const
+    {
+        return std::tie(dev, D, theta_bits) < std::tie(o.dev, o.D, o.theta_bits);
+    }
+};
+std::map<TableKey, attn::RopeTable> g_tables;
+std::vector<std::pair<int, void *>> g_retired;
+
+int get_table(int dev, int D, float theta, int S, const float **out)
+{
+    uint32_t bits;
+    std::memcpy(&bits, &theta, sizeof bits);
+    std::lock_guard<std::mutex> lk(g_mu);
+    attn::RopeTable &t = g_tables[TableKey{dev, D, bits}];
+    if (t.cs != nullptr && t.capacity >= S) {
+        *out = t.cs;
+        return ATTN_OK;
+    }
+    const int cap = ((S + 1023) / 1024) * 1024;
+    const int PG = D / 16;
+    std::vector<float> host((size_t)cap * PG * 16);
+    const double th = (double)theta;
+    for (int r = 0; r < D / 2; ++r) {
+        const double inv_freq = std::pow(th, -2.0 * (double)r / (double)D);
+        const int grp = r / 8, e = r % 8;
+        for (int p = 0; p < cap; ++p) {
+            const double ang = (double)p * inv_freq;
+            float *dst = &host[((size_t)p * PG + grp) * 16];
+            dst[e] = (float)std::cos(ang);
+            dst[8 + e] = (float)std::sin(ang);
+        }
+    }
+    void *dptr = nullptr;
+    if (hipMalloc(&dptr, host.size() * sizeof(float)) != hipSuccess) {
+        (void)hipGetLastError();
+        return ATTN_ENOMEM;
+    }
+    if (hipMemcpy(dptr, host.data(), host.size() * sizeof(float), hipMemcpyHostToDevice) != hipSuccess) {
+        (void)hipFree(dptr);
+        return ATTN_ELAUNCH;
+    }
+    if (t.cs != nullptr) g_retired.emplace_back(dev, const_cast<float *>(t.cs));
+    t.cs = static_cast<const float *>(dptr);
+    t.capacity = cap;
+    *out = t.cs;
+    return ATTN_OK;
+}
+
+int check_window(const int32_t *w, int D, int causal)
+{
+    if (w == nullptr) return ATTN_OK;
+    if (!causal) return ATTN_EINVAL;
+    if (D / 2 > attn::kMaxPairs) return ATTN_EUNSUPPORTED;
+    for (int r = 0; r + 1 < D / 2; ++r)
+        if (w[r + 1] < w[r]) return ATTN_EINVAL;
+    return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *attn_strerror(int status)
+{
+    switch (status) {
+    case ATTN_OK: return "success";
+    case ATTN_EINVAL: return "invalid argument";
+    case ATTN_EUNSUPPORTED: return "unsupported configuration (head dimension must be 64 or 128)";
+    case ATTN_EALIGN: return "tensor pointer not 16-byte aligned";
+    case ATTN_ENOMEM: return "device allocation failed";
+    case ATTN_ELAUNCH: return "HIP runtime error while launching or copying";
+    case ATTN_ENODEVICE: return "no gfx950 HIP device is current";
+    default: return "unknown status";
+    }
+}
+
+int attn_check_args(const void *q, const void *k, const void *v, const void *o, int B, int Hq, int Hkv,
+                    int S, int D, float rope_theta, int causal, float scale, const int32_t *window_table)
+{
+    int st = check_shapes(B, Hq, Hkv, S, D);
+    if (st != ATTN_OK) return st;
+    if (!q || !k || !v || !o) return ATTN_EINVAL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_EALIGN;
+    if (causal != 0 && causal != 1) return ATTN_EINVAL;
+    if (!std::isfinite(scale) || !(scale > 0.0f)) return ATTN_EINVAL;
+    st = check_theta(rope_theta);
+    if (st != ATTN_OK) return st;
+    const size_t nq = (size_t)B * S * Hq * D * 2, nkv = (size_t)B * S * Hkv * D * 2;
+    if (overlaps(o, nq, q, nq) || overlaps(o, nq, k, nkv) || overlaps(o, nq, v, nkv)) return ATTN_EINVAL;
+    return check_window(window_table, D, causal);
+}
+
+int attn_fwd(const void *q, const void *k, const void *v, void *o, int B, int Hq, int Hkv, int S, int D,
+             float rope_theta, int causal, float scale, const int32_t *window_table, void *stream)
+{
+    int st = attn_check_args(q, k, v, o, B, Hq, Hkv, S, D, rope_theta, causal, scale, window_table);
+    if (st != ATTN_OK) return st;
+    int dev = -1;
+    st = current_device_ok(&dev);
+    if (st != ATTN_OK) return st;
+    if (B == 0 || S == 0) return ATTN_OK;
+
+    attn::FwdArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.q = static_cast<const uint16_t *>(q);
+    a.k = static_cast<const uint16_t *>(k);
+    a.v = static_cast<const uint16_t *>(v);
+    a.o = static_cast<uint16_t *>(o);
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.S = S; a.D = D;
+    a.causal = causal;
+    a.scale_log2e = (float)((double)scale * 1.4426950408889634073599246810019);
+    if (window_table) {
+        a.use_window = 1;
+        for (int r = 0; r < D / 2; ++r) a.window[r] = window_table[r];
+    }
+    if (rope_theta != 0.0f) {
+        st = get_table(dev, D, rope_theta, S, &a.rope_cs);
+        if (st != ATTN_OK) return st;
+    }
+    if (attn::launch_attn_fwd(a, static_cast<hipStream_t>(stream)) != hipSuccess) return ATTN_ELAUNCH;
+    return ATTN_OK;
+}
+
+int attn_rope_apply(const void *q, const void *k, void *q_out, void *k_out, int B, int Hq, int Hkv, int S,
+                    int D, float rope_theta, void *stream)
+{
+    int st = check_shapes(B, Hq, Hkv, S, D);
+    if (st != ATTN_OK) return st;
+    if (!q || !k || !q_out || !k_out) return ATTN_EINVAL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(q_out) || !aligned16(k_out)) return ATTN_EALIGN;
+    if (rope_theta == 0.0f || check_theta(rope_theta) != ATTN_OK) return ATTN_EINVAL;
+    const size_t nq = (size_t)B * S * Hq * D * 2, nk = (size_t)B * S * Hkv * D * 2;
+    if (overlaps(q_out, nq, q, nq) || overlaps(q_out, nq, k, nk) || overlaps(k_out, nk, q, nq) ||
+        overlaps(k_out, nk, k, nk) || overlaps(q_out, nq, k_out, nk))
+        return ATTN_EINVAL;
+    int dev = -1;
+    st = current_device_ok(&dev);
+    if (st != ATTN_OK) return st;
+    if (B == 0 || S == 0) return ATTN_OK;
+    attn::RopeArgs a;
+    a.q = static_cast<const uint16_t *>(q);
+    a.k = static_cast<const uint16_t *>(k);
+    a.q_out = static_cast<uint16_t *>(q_out);
+    a.k_out = static_cast<uint16_t *>(k_out);
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.S = S; a.D = D;
+    st = get_table(dev, D, rope_theta, S, &a.rope_cs);
+    if (st != ATTN_OK) return st;
+    if (attn::launch_rope_pass(a, static_cast<hipStream_t>(stream)) != hipSuccess) return ATTN_ELAUNCH;
+    return ATTN_OK;
+}
+
+int attn_window_table(double rope_theta, int D, double k_turns, int32_t *out_host)
+{
+    if (!out_host || D <= 0 || (D % 2) != 0) return ATTN_EINVAL;
+    if (!std::isfinite(rope_theta) || !(rope_theta > 1.0) || !std::isfinite(k_turns) || !(k_turns > 0.0))
+        return ATTN_EINVAL;
+    // Pair r turns by theta^(-2r/D) per position, so one full turn takes the
+    // wavelength 2*pi*theta^(2r/D) positions; the window keeps k_turns of them.
+    const double pi = 3.14159265358979323846264338327950288;
+    for (int r = 0; r < D / 2; ++r) {
+        const double wavelength = 2.0 * pi * std::pow(rope_theta, 2.0 * (double)r / (double)D);
+        const double w = std::floor(k_turns * wavelength);
+        out_host[r] = (w >= 2147483647.0) ? 2147483647 : (int32_t)w;
+    }
+    return ATTN_OK;
+}
+
+int attn_pruned_terms(const int32_t *w_host, int D, int S, long long *per_head_out)
+{
+    if (!w_host || !per_head_out || D <= 0 || (D % 2) != 0 || S < 0) return ATTN_EINVAL;
+    // Distance d = n - m occurs S - d times in the causal triangle; pair r is
+    // removed at every distance above w[r], i.e. from d0 = w[r] + 1 to S - 1:
+    // (S - d0) + ... + 1 cells.
+    long long total = 0;
+    for (int r = 0; r < D / 2; ++r) {
+        long long d0 = (long long)w_host[r] + 1;
+        if (d0 < 0) d0 = 0;
+        if (d0 >= S) continue;
+        const long long len = (long long)S - d0;
+        total += len * (len + 1) / 2;
+    }
+    *per_head_out = total;
+    return ATTN_OK;
+}
+
+void attn_release(void)
+{
+    std::lock_guard<std::mutex> lk(g_mu);
+    int cur = -1;
+    (void)hipGetDevice(&cur);
+    auto free_on = [](int dev, void *p) {
+        if (hipSetDevice(dev) == hipSuccess) (void)hipFree(p);
+    };
+    for (auto &kv : g_tables)
+        if (kv.second.cs) free_on(kv.first.dev, const_cast<float *>(kv.second.cs));
+    for (auto &r : g_retired) free_on(r.first, r.second);
+    g_tables.clear();
+    g_retired.clear();
+    if (cur >= 0) (void)hipSetDevice(cur);
+}
+
+}  // extern "C"

@@ -1,0 +1,128 @@
+/*
+ * attn.h -- C ABI of the MI355X (gfx950) fused causal RoPE attention forward.
+ *
+ * The library computes, for every batch b, query head hq and query row n,
+ *
+ *   O[b,n,hq,:] = sum_m softmax_m( scale * <R(n) q[b,n,hq,:], R(m) k[b,m,hk,:]> ) v[b,m,hk,:]
+ *
+ * with hk = hq / (Hq / Hkv) (grouped-query heads), m ranging over 0..n under
+ * the causal mask (over 0..S-1 otherwise), and R(p) the rotary position
+ * embedding in the NeoX convention: dimension pair r = (r, r + D/2) turned by
+ * the angle p * rope_theta^(-2r/D) ("AttnFuse: A Composable DSL for Compiling
+ * Attentions to Fused GPU Kernels", section 2 "Rotary Position Embeddings"
+ * and section 4.1 "Fused RoPE").  The softmax is evaluated tile by tile with
+ * the online recurrence (running max m, denominator l, rescale
+ * alpha = exp2((m_old - m_new) * scale * log2 e), O += P V, one division by l
+ * at the end), so no S x S score matrix is ever written to memory ("Flash
+ * Attention: Causal Prefill D=128", "Online softmax: what must remain
+ * invariant").
+ *
+ * Conventions shared by every entry point:
+ *  - Tensors are bf16, contiguous [B, S, H, D] ("BSHD"); q and o have Hq
+ *    heads, k and v have Hkv heads.  Device pointers are owned by the caller
+ *    (PyTorch allocates them); the library never frees them.  Every tensor
+ *    pointer must be 16-byte aligned.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Work is enqueued asynchronously; no entry point synchronises the
+ *    stream.  Kernel faults surface at the caller's next synchronisation.
+ *  - All arguments are validated on the host before anything is enqueued;
+ *    on error nothing is launched and a negative attn_status is returned.
+ *  - Calls on one device from several host threads are safe; the library's
+ *    only shared state is its cache of RoPE cos/sin tables, guarded by a
+ *    mutex.
+ */
+#ifndef ATTN_MI355X_ATTN_H
+#define ATTN_MI355X_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_EINVAL = -1,       /* bad argument (NULL, negative size, Hq % Hkv, scale, ...) */
+    ATTN_EUNSUPPORTED = -2, /* valid but not built: D not in {64, 128} */
+    ATTN_EALIGN = -3,       /* a tensor pointer is not 16-byte aligned */
+    ATTN_ENOMEM = -4,       /* device allocation of the cos/sin table failed */
+    ATTN_ELAUNCH = -5,      /* the HIP runtime refused the launch or a copy */
+    ATTN_ENODEVICE = -6     /* no HIP device / the current device is not gfx950 */
+} attn_status;
+
+/*
+ * Fused causal attention forward with RoPE applied to the Q and K tiles as
+ * they are staged on chip.
+ *
+ *  q [B,S,Hq,D], k/v [B,S,Hkv,D], o [B,S,Hq,D]: bf16 device pointers.  o must
+ *      not overlap q, k or v.
+ *  B >= 0, S >= 0 (either being 0 is a no-op), Hq >= 1, Hkv >= 1,
+ *      Hq % Hkv == 0, D in {64, 128}.
+ *  rope_theta: > 1 rotates Q and K (positions 0..S-1); 0 disables RoPE (the
+ *      inputs are used as given).  Other values are rejected.
+ *  causal: 1 keeps keys m <= n, 0 keeps all keys.
+ *  scale: finite and > 0; multiplies q.k (natural-log softmax domain; the
+ *      kernel folds log2 e into it itself).
+ *  window_table: NULL, or a HOST array of D/2 int32 per-pair distance limits
+ *      w[r], non-decreasing in r.  Pair r then contributes to score (n, m)
+ *      only when n - m <= w[r] ("ATFlash -- Per-RoPE-Wavelength Attention
+ *      Windows", "The idea").  Requires causal == 1 and D/2 <= 64.  With
+ *      rope_theta == 0 the pairs are those of inputs rotated beforehand
+ *      (attn_rope_apply).  The table is copied by value into the kernel
+ *      arguments; the caller may free it when the call returns.
+ */
+int attn_fwd(const void *q, const void *k, const void *v, void *o,
+             int B, int Hq, int Hkv, int S, int D,
+             float rope_theta, int causal, float scale,
+             const int32_t *window_table, void *stream);
+
+/*
+ * The separate RoPE pass ("AttnFuse", section 1 and Figure 1(a): rotate Q
+ * and K in their own kernel, then run plain attention): writes the rotated
+ * q_out [B,S,Hq,D] and k_out [B,S,Hkv,D] (bf16, rounded to nearest even from
+ * the same fp32 arithmetic the fused kernel uses, so that
+ * attn_rope_apply + attn_fwd(rope_theta = 0) reproduces attn_fwd with RoPE
+ * bit for bit).  q_out/k_out are caller-owned workspaces that must not
+ * overlap the inputs.  rope_theta must be > 1.
+ */
+int attn_rope_apply(const void *q, const void *k, void *q_out, void *k_out,
+                    int B, int Hq, int Hkv, int S, int D, float rope_theta,
+                    void *stream);
+
+/*
+ * Host-only: the per-pair window table w[r] = floor(k_turns * 2*pi *
+ * rope_theta^(2r/D)), r = 0..D/2-1, evaluated in fp64 (pair r's wavelength
+ * times the number of full turns; "ATFlash", "The idea").  Values beyond
+ * INT32_MAX saturate.  out_host holds D/2 int32.  rope_theta > 1, k_turns > 0,
+ * D even and positive.
+ */
+int attn_window_table(double rope_theta, int D, double k_turns, int32_t *out_host);
+
+/*
+ * Host-only: the number of (query, key, pair) terms the window removes from
+ * one head's causal triangle 0 <= m <= n < S, i.e. sum over r of the cells
+ * with n - m > w[r].  Exact int64 closed form.  w_host holds D/2 int32.
+ */
+int attn_pruned_terms(const int32_t *w_host, int D, int S, long long *per_head_out);
+
+/*
+ * Host-only validation of an attn_fwd argument list, without touching the
+ * device (pointers are checked for NULL and alignment only).  Returns the
+ * status attn_fwd would return before launching.
+ */
+int attn_check_args(const void *q, const void *k, const void *v, const void *o,
+                    int B, int Hq, int Hkv, int S, int D, float rope_theta,
+                    int causal, float scale, const int32_t *window_table);
+
+/* A static English description of a status code. */
+const char *attn_strerror(int status);
+
+/* Frees the cached cos/sin tables on every device.  Not to be called while
+ * work that uses them may still be running. */
+void attn_release(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_MI355X_ATTN_H */
