@@ -156,14 +156,16 @@ int attn_check_args(const void *q, const void *k, const void *v, const void *o, 
 {
     int st = check_shapes(B, Hq, Hkv, S, D);
     if (st != ATTN_OK) return st;
-    if (!q || !k || !v || !o) return ATTN_EINVAL;
+    const bool empty = (B == 0 || S == 0);  // nothing is read or written: pointers may be NULL
+    if (!empty && (!q || !k || !v || !o)) return ATTN_EINVAL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_EALIGN;
     if (causal != 0 && causal != 1) return ATTN_EINVAL;
     if (!std::isfinite(scale) || !(scale > 0.0f)) return ATTN_EINVAL;
     st = check_theta(rope_theta);
     if (st != ATTN_OK) return st;
     const size_t nq = (size_t)B * S * Hq * D * 2, nkv = (size_t)B * S * Hkv * D * 2;
-    if (overlaps(o, nq, q, nq) || overlaps(o, nq, k, nkv) || overlaps(o, nq, v, nkv)) return ATTN_EINVAL;
+    if (!empty && (overlaps(o, nq, q, nq) || overlaps(o, nq, k, nkv) || overlaps(o, nq, v, nkv)))
+        return ATTN_EINVAL;
     return check_window(window_table, D, causal);
 }
 
@@ -203,12 +205,13 @@ int attn_rope_apply(const void *q, const void *k, void *q_out, void *k_out, int 
 {
     int st = check_shapes(B, Hq, Hkv, S, D);
     if (st != ATTN_OK) return st;
-    if (!q || !k || !q_out || !k_out) return ATTN_EINVAL;
+    const bool empty = (B == 0 || S == 0);
+    if (!empty && (!q || !k || !q_out || !k_out)) return ATTN_EINVAL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(q_out) || !aligned16(k_out)) return ATTN_EALIGN;
     if (rope_theta == 0.0f || check_theta(rope_theta) != ATTN_OK) return ATTN_EINVAL;
     const size_t nq = (size_t)B * S * Hq * D * 2, nk = (size_t)B * S * Hkv * D * 2;
-    if (overlaps(q_out, nq, q, nq) || overlaps(q_out, nq, k, nk) || overlaps(k_out, nk, q, nq) ||
-        overlaps(k_out, nk, k, nk) || overlaps(q_out, nq, k_out, nk))
+    if (!empty && (overlaps(q_out, nq, q, nq) || overlaps(q_out, nq, k, nk) || overlaps(k_out, nk, q, nq) ||
+                   overlaps(k_out, nk, k, nk) || overlaps(q_out, nq, k_out, nk)))
         return ATTN_EINVAL;
     int dev = -1;
     st = current_device_ok(&dev);

@@ -147,7 +147,7 @@ __device__ __forceinline__ void window_chunk(const FwdArgs &a, bf16x8_t ka, bf16
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int m = mk0 + 8 * (i >> 2) + 4 * g + (i & 3);
-            if (n - m <= w) acc[i] += part[i];
+            acc[i] += (n - m <= w) ? part[i] : 0.0f;
         }
     }
 }
@@ -160,7 +160,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    // Wave index read through readfirstlane: the compiler then knows every
+    // quantity derived from it (row ranges, tile skips, window decisions) is
+    // wave-uniform and branches on scalars instead of masking lanes.
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31;
     const int g = lane >> 5;
 

@@ -82,12 +82,14 @@ def test_check_args_accepts_valid():
     assert _chk(rope_theta=0.0) == binding.ATTN_OK
     assert _chk(D=64, Hq=8, Hkv=1) == binding.ATTN_OK
     assert _chk(S=0) == binding.ATTN_OK and _chk(B=0) == binding.ATTN_OK
+    assert _chk(S=0, q=0, k=0, v=0, o=0) == binding.ATTN_OK  # empty tensors may have NULL data
     assert _chk(causal=0) == binding.ATTN_OK
     assert _chk(window_table=O.window_table(5e5, 128, 2.0)) == binding.ATTN_OK
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(q=0), binding.ATTN_EINVAL),
+    (dict(q=0, S=16), binding.ATTN_EINVAL),
     (dict(o=0), binding.ATTN_EINVAL),
     (dict(q=A + 8), binding.ATTN_EALIGN),
     (dict(v=A * 128 + 2), binding.ATTN_EALIGN),
