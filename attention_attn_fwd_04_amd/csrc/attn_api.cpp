@@ -36,6 +36,10 @@ int check_shapes(int B, int Hq, int Hkv, int S, int D)
     if (rows > (1LL << 40)) return ATTN_EINVAL;
     const long long q_tiles = ((long long)S + 255) / 256;
     if (q_tiles * Hq * (long long)B > 0x7fffffffLL) return ATTN_EINVAL;
+    // The kernels address one head's rows (and the cos/sin table) through
+    // 32-bit buffer offsets.
+    const long long head_span = (long long)S * (Hq > Hkv ? Hq : Hkv) * D * 2;
+    if (head_span > 0x7fffffffLL || (long long)S * D * 4 > 0x7fffffffLL) return ATTN_EUNSUPPORTED;
     return ATTN_OK;
 }
 
