@@ -39,7 +39,7 @@ int check_shapes(int B, int Hq, int Hkv, int S, int D)
     // The kernels address one head's rows (and the cos/sin table) through
     // 32-bit buffer offsets.
     const long long head_span = (long long)S * (Hq > Hkv ? Hq : Hkv) * D * 2;
-    if (head_span > 0x7fffffffLL || (long long)S * D * 4 > 0x7fffffffLL) return ATTN_EUNSUPPORTED;
+    if (head_span > 0x7fffffffLL || (long long)S * D * 2 > 0x7fffffffLL) return ATTN_EUNSUPPORTED;
     return ATTN_OK;
 }
 
@@ -87,7 +87,31 @@ struct TableKey {
 std::map<TableKey, attn::RopeTable> g_tables;
 std::vector<std::pair<int, void *>> g_retired;
 
-int get_table(int dev, int D, float theta, int S, const float **out)
+// Round a value in [-1, 1] from fp64 to the nearest fp16 (ties to even),
+// returning its bit pattern.  One rounding step: the value is scaled by the
+// fp16 quantum of its binade (2^-24 in the subnormal range) and rounded there.
+uint16_t fp16_bits_rne(double x)
+{
+    if (x == 0.0) return std::signbit(x) ? 0x8000u : 0u;
+    int e;
+    std::frexp(x, &e);                  // |x| = m * 2^e, 0.5 <= m < 1
+    int qexp = e - 11;                  // 11 significant bits
+    if (qexp < -24) qexp = -24;         // subnormal quantum
+    const double q = std::ldexp(1.0, qexp);
+    const double r = std::nearbyint(x / q) * q;  // exact scaling, RNE rounding
+    const float f = (float)r;           // exactly representable in fp16 and fp32
+    uint32_t u;
+    std::memcpy(&u, &f, sizeof u);
+    const uint32_t sign = (u >> 16) & 0x8000u;
+    const int fe = (int)((u >> 23) & 0xff) - 127;
+    const uint32_t mant = u & 0x7fffffu;
+    if (fe >= -14) return (uint16_t)(sign | ((uint32_t)(fe + 15) << 10) | (mant >> 13));
+    // subnormal fp16: value = mant' * 2^-24
+    const uint32_t full = (mant | 0x800000u) >> (-14 - fe);
+    return (uint16_t)(sign | (full >> 13));
+}
+
+int get_table(int dev, int D, float theta, int S, const uint16_t **out)
 {
     uint32_t bits;
     std::memcpy(&bits, &theta, sizeof bits);
@@ -99,29 +123,29 @@ int get_table(int dev, int D, float theta, int S, const float **out)
     }
     const int cap = ((S + 1023) / 1024) * 1024;
     const int PG = D / 16;
-    std::vector<float> host((size_t)cap * PG * 16);
+    std::vector<uint16_t> host((size_t)cap * PG * 16);
     const double th = (double)theta;
     for (int r = 0; r < D / 2; ++r) {
         const double inv_freq = std::pow(th, -2.0 * (double)r / (double)D);
         const int grp = r / 8, e = r % 8;
         for (int p = 0; p < cap; ++p) {
             const double ang = (double)p * inv_freq;
-            float *dst = &host[((size_t)p * PG + grp) * 16];
-            dst[e] = (float)std::cos(ang);
-            dst[8 + e] = (float)std::sin(ang);
+            // quarter 0 holds the cosines, quarter 1 the sines (see attn::RopeTable)
+            host[(((size_t)p * 2 + 0) * PG + grp) * 8 + e] = fp16_bits_rne(std::cos(ang));
+            host[(((size_t)p * 2 + 1) * PG + grp) * 8 + e] = fp16_bits_rne(std::sin(ang));
         }
     }
     void *dptr = nullptr;
-    if (hipMalloc(&dptr, host.size() * sizeof(float)) != hipSuccess) {
+    if (hipMalloc(&dptr, host.size() * sizeof(uint16_t)) != hipSuccess) {
         (void)hipGetLastError();
         return ATTN_ENOMEM;
     }
-    if (hipMemcpy(dptr, host.data(), host.size() * sizeof(float), hipMemcpyHostToDevice) != hipSuccess) {
+    if (hipMemcpy(dptr, host.data(), host.size() * sizeof(uint16_t), hipMemcpyHostToDevice) != hipSuccess) {
         (void)hipFree(dptr);
         return ATTN_ELAUNCH;
     }
-    if (t.cs != nullptr) g_retired.emplace_back(dev, const_cast<float *>(t.cs));
-    t.cs = static_cast<const float *>(dptr);
+    if (t.cs != nullptr) g_retired.emplace_back(dev, const_cast<uint16_t *>(t.cs));
+    t.cs = static_cast<const uint16_t *>(dptr);
     t.capacity = cap;
     *out = t.cs;
     return ATTN_OK;
@@ -276,7 +300,7 @@ void attn_release(void)
         if (hipSetDevice(dev) == hipSuccess) (void)hipFree(p);
     };
     for (auto &kv : g_tables)
-        if (kv.second.cs) free_on(kv.first.dev, const_cast<float *>(kv.second.cs));
+        if (kv.second.cs) free_on(kv.first.dev, const_cast<uint16_t *>(kv.second.cs));
     for (auto &r : g_retired) free_on(r.first, r.second);
     g_tables.clear();
     g_retired.clear();

@@ -68,33 +68,28 @@ struct Geo {
     static constexpr int PG = D / 16;       // 8-pair groups per row
     static constexpr int DB = D / 32;       // 32-row blocks of O^T
     static constexpr int CH = D / 8;        // 16-byte chunks per row
-    static constexpr int ROWB = D * 2;      // bytes per row (unpadded)
-    static constexpr int K_BYTES = kBN * ROWB;
-    static constexpr int V_BYTES = kBN * ROWB;
-    static constexpr int BUF_BYTES = K_BYTES + V_BYTES;
-    static constexpr int Q_BYTES = kBM * ROWB;
-    static constexpr int LDS_BYTES = (2 * BUF_BYTES > Q_BYTES) ? 2 * BUF_BYTES : Q_BYTES;
-    static constexpr int K_UNITS = kBN * PG;          // (key, pair group)
-    static constexpr int V_UNITS = kBN * CH;          // (key, 16-byte chunk)
-    static constexpr int V_PER_THREAD = (V_UNITS + kThreads - 1) / kThreads;
-    static_assert(K_UNITS <= kThreads, "at most one K unit per thread");
-    static_assert(V_UNITS % kThreads == 0 || V_UNITS < kThreads, "V units split evenly");
+    static constexpr int ROWB = D * 2;      // bytes per K / V row in LDS (unpadded)
+    static constexpr int TILE_B = kBN * ROWB;             // one K or V tile
+    static constexpr int NI = TILE_B / 1024;              // 1 KB direct-load instructions per tile
+    static constexpr int NI_W = NI / kWaves;               // ... per wave
+    static constexpr int RPI = 1024 / ROWB;               // rows per direct-load instruction
+    static constexpr int KRING = 0, VRING = 3 * TILE_B;   // 3-slot rings for K and V
+    static constexpr int RING_BYTES = 6 * TILE_B;
+    static constexpr int QP_B = ROWB + 16;                // padded Q staging rows
+    static constexpr int Q_BYTES = kBM * QP_B;
+    static constexpr int LDS_BYTES = (RING_BYTES > Q_BYTES) ? RING_BYTES : Q_BYTES;
+    static constexpr int K_UNITS = kBN * PG;              // (key, pair group) rotation units
+    static_assert(NI % kWaves == 0, "direct-load instructions split over the waves");
 
-    // Swizzled byte offset of 16-byte chunk c of row r in a K or Q tile:
-    // 16 consecutive rows read at one logical chunk land in 16 distinct
-    // 4-bank groups.
-    static __device__ __forceinline__ int k_off(int r, int c)
-    {
-        if constexpr (D == 128) return r * ROWB + ((c ^ (r & 15)) << 4);
-        else return r * ROWB + ((c ^ ((r >> 1) & 7)) << 4);
-    }
-    // Swizzled byte offset of chunk c of row r in a V tile: the 4 rows x 4
-    // chunks read by one half-wave of ds_read_b64_tr_b16 cover all banks.
-    static __device__ __forceinline__ int v_off(int r, int c)
-    {
-        if constexpr (D == 128) return r * ROWB + ((c ^ ((r & 3) << 2)) << 4);
-        else return r * ROWB + ((c ^ (((r >> 1) & 1) << 2)) << 4);
-    }
+    // K tiles are stored as rows of ROWB bytes whose 16-byte chunks are
+    // XOR-permuted per row: 16 lanes reading one logical chunk of 16
+    // consecutive rows hit 16 distinct 4-bank groups.
+    static __device__ __forceinline__ int kx(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+    static __device__ __forceinline__ int k_off(int r, int c) { return r * ROWB + ((c ^ kx(r)) << 4); }
+    // V tiles: the 4 rows x 64 bytes half a wave of ds_read_b64_tr_b16 reads
+    // land on distinct banks.
+    static __device__ __forceinline__ int vx(int r) { return D == 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2); }
+    static __device__ __forceinline__ int v_off(int r, int c) { return r * ROWB + ((c ^ vx(r)) << 4); }
 };
 
 // v_permlane32_swap exchanges lanes 0..31 of one register with lanes 32..63
@@ -130,6 +125,30 @@ __device__ __forceinline__ float4 bload16f(__amdgpu_buffer_rsrc_t r, uint32_t of
 
 template <typename T>
 __device__ __forceinline__ T &lds_at(uint8_t *base, int off) { return *reinterpret_cast<T *>(base + off); }
+
+// Buffer load of 16 bytes per lane straight into LDS: lane i writes
+// lds_base + 16 i (lds_base wave-uniform, passed in M0).  Out-of-range lanes
+// write zeros.  Issued through inline assembly so that the compiler does not
+// treat these asynchronous LDS writes as pending on every later LDS read and
+// barrier; the kernel waits for them itself (wait_vmcnt) before the barrier
+// that publishes the tile.  One wait state separates the M0 write from its use.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, const uint8_t *lds_base)
+{
+    const uint32_t m0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)lds_base;
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(r), "s"(m0)
+                 : "memory", "m0");
+}
+
+// s_waitcnt on the vector-memory counter only: at most n loads of this wave
+// still in flight (loads retire in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
 
 // ---------------------------------------------------------------------------
 // Per-pair distance window on one 32-key x 32-query block and one MFMA
@@ -227,7 +246,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
     const __amdgpu_buffer_rsrc_t q_rs = make_rsrc(a.q + ((size_t)b * S * a.Hq + hq) * D, (uint32_t)S * q_rowb);
     const __amdgpu_buffer_rsrc_t k_rs = make_rsrc(a.k + ((size_t)b * S * a.Hkv + hk) * D, (uint32_t)S * kv_rowb);
     const __amdgpu_buffer_rsrc_t v_rs = make_rsrc(a.v + ((size_t)b * S * a.Hkv + hk) * D, (uint32_t)S * kv_rowb);
-    const __amdgpu_buffer_rsrc_t cs_rs = make_rsrc(a.rope_cs, ROPE ? (uint32_t)S * G::PG * 64u : 0u);
+    const __amdgpu_buffer_rsrc_t cs_rs = make_rsrc(a.rope_cs, ROPE ? (uint32_t)S * G::PG * 32u : 0u);
     uint16_t *og = a.o + ((size_t)b * S * a.Hq + hq) * D;
 
     // ---- Q tile: load, rotate, stage through LDS into B-operand registers --
@@ -237,85 +256,104 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
         uint4 lo = bload16(q_rs, n * q_rowb + 16u * pg);
         uint4 hi = bload16(q_rs, n * q_rowb + (uint32_t)D + 16u * pg);
         if constexpr (ROPE) {
-            float cs[16];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float4 t = bload16f(cs_rs, (n * G::PG + pg) * 64u + 16u * i);
-                cs[4 * i] = t.x; cs[4 * i + 1] = t.y; cs[4 * i + 2] = t.z; cs[4 * i + 3] = t.w;
-            }
-            rope_rotate8(lo, hi, cs);
+            const uint4 cq = bload16(cs_rs, ((n * 2u + 0) * G::PG + pg) * 16u);
+            const uint4 sq = bload16(cs_rs, ((n * 2u + 1) * G::PG + pg) * 16u);
+            rope_rotate8(lo, hi, cq, sq);
         }
-        lds_at<uint4>(smem, G::k_off(row, pg)) = lo;
-        lds_at<uint4>(smem, G::k_off(row, G::PG + pg)) = hi;
+        lds_at<uint4>(smem, row * G::QP_B + 16 * pg) = lo;
+        lds_at<uint4>(smem, row * G::QP_B + 16 * (G::PG + pg)) = hi;
     }
     __syncthreads();
     bf16x8_t qreg[G::KCH];
 #pragma unroll
     for (int kc = 0; kc < G::KCH; ++kc)
-        qreg[kc] = lds_at<bf16x8_t>(smem, G::k_off(wave * kRowsPerWave + l32, kc + G::PG * g));
+        qreg[kc] = lds_at<bf16x8_t>(smem, (wave * kRowsPerWave + l32) * G::QP_B + 16 * (kc + G::PG * g));
     __syncthreads();
 
     // ---- key range ----------------------------------------------------------
     const int kv_end = CAUSAL ? min(S, n0 + kBM) : S;
-    const int n_tiles = (kv_end + kBN - 1) / kBN;
+    const int T = (kv_end + kBN - 1) / kBN;              // key tiles of the work-group
     const int nw0 = n0 + wave * kRowsPerWave;            // first query of this wave
     const bool wave_active = nw0 < S;
     const int wave_kv_end = CAUSAL ? min(S, nw0 + kRowsPerWave) : S;
+    const int wave_tiles = wave_active ? (wave_kv_end + kBN - 1) / kBN : 0;
     const float c = a.scale_log2e;
 
-    // ---- staging ---------------------------------------------------------
-    const bool k_thread = tid < G::K_UNITS;
-    const int k_key = tid / G::PG, k_pg = tid - (tid / G::PG) * G::PG;
-    uint4 k_lo = make_uint4(0, 0, 0, 0), k_hi = k_lo;
-    float k_cs[16];
+    // ---- ping-pong schedule ----------------------------------------------------
+    // The 8 waves form two groups, A = waves 0..3 and B = waves 4..7, one wave
+    // of each on every SIMD.  Each wave alternates a matrix phase (PV of the
+    // previous tile, then the scores of the current tile: 32 MFMAs) and a
+    // vector phase (mask, online softmax and P packing of the current tile,
+    // and, with RoPE, rotating its share of the next K tile into LDS).  Two
+    // barriers per period keep the groups half a period apart, so on every
+    // SIMD one wave's vector phase runs under the other wave's MFMAs:
+    //
+    //   period j:      [Y(j-1) .. X(j)]           [X(j) .. Y(j)]
+    //   group A:   PV(j-1), QK(j)              softmax(j)
+    //   group B:   softmax(j-1)                PV(j-1), QK(j)
+    //
+    // During period j only K(j) and V(j-1) are read.  K and V tiles live in
+    // 3-slot rings (tile t in slot t % 3).  V(j+1) and, without RoPE, K(j+2)
+    // are fetched with buffer loads straight into LDS during period j (each
+    // wave issues 1 KB per tile) and each wave waits for its own copies just
+    // before barrier Y(j+1); with RoPE, K(j+1) is loaded into registers,
+    // rotated and written during period j.
+    const int grp = wave >> 2;
+    auto kslot = [&](int t) __attribute__((always_inline)) { return smem + G::KRING + (t % 3) * G::TILE_B; };
+    auto vslot = [&](int t) __attribute__((always_inline)) { return smem + G::VRING + (t % 3) * G::TILE_B; };
+
+    // Direct loads of this wave's share of a K or V tile: instructions
+    // wave + 8 i, each 1 KB = RPI rows; lane l writes chunk slot l % CH of row
+    // l / CH, i.e. the global chunk (slot ^ swizzle(row)).
+    const int dl_row = lane / G::CH, dl_slot = lane % G::CH;
+    auto dload_k = [&](int t) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) k_cs[i] = 0.f;
-    uint4 v_r[G::V_PER_THREAD];
+        for (int i = 0; i < G::NI_W; ++i) {
+            const int ins = wave + kWaves * i;
+            const int r = ins * G::RPI + dl_row;
+            const uint32_t off = (uint32_t)(t * kBN + r) * kv_rowb + 16u * (uint32_t)(dl_slot ^ G::kx(r));
+            dma16(k_rs, off, kslot(t) + ins * 1024);
+        }
+    };
+    auto dload_v = [&](int t) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < G::NI_W; ++i) {
+            const int ins = wave + kWaves * i;
+            const int r = ins * G::RPI + dl_row;
+            const uint32_t off = (uint32_t)(t * kBN + r) * kv_rowb + 16u * (uint32_t)(dl_slot ^ (G::vx(r) >> 0));
+            dma16(v_rs, off, vslot(t) + ins * 1024);
+        }
+    };
+
+    // RoPE path: each group rotates half of the K tile (thread tg of the group
+    // owns unit tg + 256 grp: one key's 8-pair group).
+    const int tg = tid & 255;
+    const int k_unit = tg + 256 * grp;
+    const int k_key = k_unit / G::PG, k_pg = k_unit % G::PG;
+    uint4 k_lo = make_uint4(0, 0, 0, 0), k_hi = k_lo, k_cq = k_lo, k_sq = k_lo;
 
     // Smallest query-key distance in the work-group's tile starting at key m0:
     // a pair group whose widest window is below it is pruned everywhere in
     // the tile, so its K columns are neither loaded nor rotated.
-    auto group_pruned = [&](int m0, int pg) {
+    auto group_pruned = [&](int m0, int pg) __attribute__((always_inline)) {
         const int dmin = max(0, n0 - (m0 + kBN - 1));
         return WINDOW && a.window[8 * pg + 7] < dmin;
     };
-
-    auto stage_load = [&](int m0) {
-        if (k_thread && !group_pruned(m0, k_pg)) {
-            const uint32_t m = (uint32_t)(m0 + k_key);
-            k_lo = bload16(k_rs, m * kv_rowb + 16u * k_pg);
-            k_hi = bload16(k_rs, m * kv_rowb + (uint32_t)D + 16u * k_pg);
-            if constexpr (ROPE) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float4 t = bload16f(cs_rs, (m * G::PG + k_pg) * 64u + 16u * i);
-                    k_cs[4 * i] = t.x; k_cs[4 * i + 1] = t.y; k_cs[4 * i + 2] = t.z; k_cs[4 * i + 3] = t.w;
-                }
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < G::V_PER_THREAD; ++i) {
-            const int u = tid + i * kThreads;
-            if (u < G::V_UNITS) {
-                const uint32_t m = (uint32_t)(m0 + u / G::CH);
-                v_r[i] = bload16(v_rs, m * kv_rowb + 16u * (u % G::CH));
-            }
+    auto rload_k = [&](int m0, int unit, int key, int pg) __attribute__((always_inline)) {
+        if (unit < G::K_UNITS && !group_pruned(m0, pg)) {
+            const uint32_t m = (uint32_t)(m0 + key);
+            k_lo = bload16(k_rs, m * kv_rowb + 16u * pg);
+            k_hi = bload16(k_rs, m * kv_rowb + (uint32_t)D + 16u * pg);
+            k_cq = bload16(cs_rs, ((m * 2u + 0) * G::PG + pg) * 16u);
+            k_sq = bload16(cs_rs, ((m * 2u + 1) * G::PG + pg) * 16u);
         }
     };
-
-    auto stage_store = [&](int buf, int m0) {
-        uint8_t *ks = smem + buf * G::BUF_BYTES;
-        uint8_t *vs = ks + G::K_BYTES;
-        if (k_thread && !group_pruned(m0, k_pg)) {  // pruned groups are never read
+    auto rstore_k = [&](uint8_t *ks, int m0, int unit, int key, int pg) __attribute__((always_inline)) {
+        if (unit < G::K_UNITS && !group_pruned(m0, pg)) {  // pruned groups are never read
             uint4 lo = k_lo, hi = k_hi;
-            if constexpr (ROPE) rope_rotate8(lo, hi, k_cs);
-            lds_at<uint4>(ks, G::k_off(k_key, k_pg)) = lo;
-            lds_at<uint4>(ks, G::k_off(k_key, G::PG + k_pg)) = hi;
-        }
-#pragma unroll
-        for (int i = 0; i < G::V_PER_THREAD; ++i) {
-            const int u = tid + i * kThreads;
-            if (u < G::V_UNITS) lds_at<uint4>(vs, G::v_off(u / G::CH, u % G::CH)) = v_r[i];
+            rope_rotate8(lo, hi, k_cq, k_sq);
+            lds_at<uint4>(ks, G::k_off(key, pg)) = lo;
+            lds_at<uint4>(ks, G::k_off(key, G::PG + pg)) = hi;
         }
     };
 
@@ -326,116 +364,220 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc_o[db][i] = 0.f;
     float m_ref = -__builtin_inff(), l_run = 0.f;
+    f32x16_t acc_s[2];
+    bf16x8_t pf[kBN / 16];
 
-    // Transpose-read addressing for the PV A operand: within each 16-lane
-    // group, source lane s reads key (s / 4) of a 4-key group at dims
-    // D0 + 4 (s % 4) .. +3, with D0 = 32 db + 16 ((lane / 16) % 2).  Lane i
-    // of the group then holds dim D0 + i of the 4 keys.
+    // Per-lane LDS byte offsets of the MFMA operands; the tile base and the
+    // key-block / chunk terms are compile-time constants.
+    // K operand of k-step kc: row l32 (+32 for the second key block), logical
+    // chunk kc + PG g.
+    int k_addr[G::KCH];
+#pragma unroll
+    for (int kc = 0; kc < G::KCH; ++kc) k_addr[kc] = G::k_off(l32, kc + G::PG * g);
+    // PV A operand through ds_read_b64_tr_b16: within each 16-lane group,
+    // source lane s reads key (s / 4) of a 4-key group at dims D0 + 4 (s % 4)
+    // .. +3, D0 = 32 db + 16 ((lane / 16) % 2); lane i of the group then holds
+    // dim D0 + i of those 4 keys.  Key rows 16 ch + 4 g + s / 4 (+8).
     const int tr_key = (lane & 15) >> 2;
     const int tr_dim = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    int v_addr[G::DB];
+#pragma unroll
+    for (int db = 0; db < G::DB; ++db)
+        v_addr[db] = G::v_off(4 * g + tr_key, (32 * db + tr_dim) >> 3) + 2 * (tr_dim & 4);
 
-    if (n_tiles > 0) {
-        stage_load(0);
-        stage_store(0, 0);
-    }
-    __syncthreads();
-
-    for (int j = 0; j < n_tiles; ++j) {
-        const int m0 = j * kBN;
-        if (j + 1 < n_tiles) stage_load(m0 + kBN);
-        uint8_t *ks = smem + (j & 1) * G::BUF_BYTES;
-        uint8_t *vs = ks + G::K_BYTES;
-
-        if (wave_active && m0 < wave_kv_end) {
-            // S^T = K' Q'^T for two 32-key blocks x one 32-query block.
-            f32x16_t acc_s[2];
+    // S^T = K' Q'^T for the 64-key tile at m0 (two 32-key blocks).
+    auto qk = [&](const uint8_t *ks, int m0) __attribute__((always_inline)) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) acc_s[kb][i] = 0.f;
+            for (int i = 0; i < 16; ++i) acc_s[kb][i] = 0.f;
 #pragma unroll
-            for (int kc = 0; kc < G::KCH; ++kc) {
+        for (int kc = 0; kc < G::KCH; ++kc) {
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const bf16x8_t ka = lds_at<bf16x8_t>(ks, G::k_off(kb * 32 + l32, kc + G::PG * g));
-                    if constexpr (WINDOW)
-                        window_chunk(a, ka, qreg[kc], acc_s[kb], kc, nw0, m0 + kb * 32, l32, g);
-                    else
-                        acc_s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[kc], acc_s[kb], 0, 0, 0);
-                }
+            for (int kb = 0; kb < 2; ++kb) {
+                const bf16x8_t ka = lds_at<bf16x8_t>(const_cast<uint8_t *>(ks), k_addr[kc] + kb * 32 * G::ROWB);
+                if constexpr (WINDOW)
+                    window_chunk(a, ka, qreg[kc], acc_s[kb], kc, nw0, m0 + kb * 32, l32, g);
+                else
+                    acc_s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[kc], acc_s[kb], 0, 0, 0);
             }
-
-            // Mask: tiles crossing the diagonal or the sequence end.
-            const bool need_mask = (CAUSAL && m0 + kBN - 1 > nw0) || (m0 + kBN > S);
-            if (need_mask) {
-                const int n = nw0 + l32;
+        }
+        if constexpr (!WINDOW) {
+            // Keep the K operand reads PF steps ahead of the MFMAs that use
+            // them, so the LDS latency is hidden inside this wave.
+            constexpr int NM = 2 * G::KCH, PF = 4;
+            __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int m = m0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-                        const bool masked = (CAUSAL && m > n) || m >= S;
-                        acc_s[kb][i] = masked ? -__builtin_inff() : acc_s[kb][i];
-                    }
+            for (int i = 0; i < NM - PF; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
+            __builtin_amdgcn_sched_group_barrier(0x008, PF, 0);
+        }
+    };
 
-            // Online softmax, one query per lane (and its mirror lane).
-            float mx = acc_s[0][0];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, acc_s[kb][i]);
-            mx = max_halves(mx);
-            // Lazy rescale: move the reference max only when some row's max
-            // grew by more than 2^8 in probability; the decision is per wave.
-            const bool grow = (mx - m_ref) * c > kRescaleLog2;
-            if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-                const float m_new = fmaxf(m_ref, mx);
-                const float alpha = fast_exp2((m_ref - m_new) * c);
-                l_run *= alpha;
-#pragma unroll
-                for (int db = 0; db < G::DB; ++db)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) acc_o[db][i] *= alpha;
-                m_ref = m_new;
-            }
-            const float mc = m_ref * c;
-            float rs = 0.f;
+    // Mask, online-softmax update and bf16 packing of P for the tile at m0.
+    auto softmax = [&](int m0) __attribute__((always_inline)) {
+        const bool need_mask = (CAUSAL && m0 + kBN - 1 > nw0) || (m0 + kBN > S);
+        if (need_mask) {
+            const int n = nw0 + l32;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const float p = fast_exp2(__builtin_fmaf(acc_s[kb][i], c, -mc));
-                    acc_s[kb][i] = p;
-                    rs += p;
+                    const int m = m0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
+                    const bool masked = (CAUSAL && m > n) || m >= S;
+                    acc_s[kb][i] = masked ? -__builtin_inff() : acc_s[kb][i];
                 }
-            l_run += rs;
+        }
+        float mx = acc_s[0][0];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, acc_s[kb][i]);
+        mx = max_halves(mx);
+        // Lazy rescale: move the reference max only when some row's max
+        // grew by more than 2^8 in probability; the decision is per wave.
+        const bool grow = (mx - m_ref) * c > kRescaleLog2;
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+            const float m_new = fmaxf(m_ref, mx);
+            const float alpha = fast_exp2((m_ref - m_new) * c);
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc_o[db][i] *= alpha;
+            m_ref = m_new;
+        }
+        const float mc = m_ref * c;
+        float rs = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float p = fast_exp2(__builtin_fmaf(acc_s[kb][i], c, -mc));
+                acc_s[kb][i] = p;
+                rs += p;
+            }
+        l_run += rs;
+#pragma unroll
+        for (int ch = 0; ch < kBN / 16; ++ch) {
+            const int kb = ch >> 1, h8 = (ch & 1) * 8;
+            uint32_t w[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(acc_s[kb][h8 + 2 * e], acc_s[kb][h8 + 2 * e + 1]);
+            pf[ch] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
+        }
+    };
 
-            // O^T += V^T P^T over four 16-key chunks.
+    // O^T += V^T P^T over four 16-key chunks of the V tile in vs.
+    auto pv = [&](const uint8_t *vs) __attribute__((always_inline)) {
 #pragma unroll
-            for (int ch = 0; ch < kBN / 16; ++ch) {
-                const int kb = ch >> 1, h8 = (ch & 1) * 8;
-                uint32_t w[4];
+        for (int ch = 0; ch < kBN / 16; ++ch) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(acc_s[kb][h8 + 2 * e], acc_s[kb][h8 + 2 * e + 1]);
-                const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
-#pragma unroll
-                for (int db = 0; db < G::DB; ++db) {
-                    const int dim = 32 * db + tr_dim;
-                    const int key0 = 16 * ch + 4 * g + tr_key;
-                    const int off0 = G::v_off(key0, dim >> 3) + ((dim & 4) << 1);
-                    const int off1 = G::v_off(key0 + 8, dim >> 3) + ((dim & 4) << 1);
-                    const i16x4_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(vs + off0));
-                    const i16x4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(vs + off1));
-                    const uint2 u0 = __builtin_bit_cast(uint2, t0), u1 = __builtin_bit_cast(uint2, t1);
-                    const bf16x8_t va = __builtin_bit_cast(bf16x8_t, make_uint4(u0.x, u0.y, u1.x, u1.y));
-                    acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf, acc_o[db], 0, 0, 0);
-                }
+            for (int db = 0; db < G::DB; ++db) {
+                const int off0 = v_addr[db] + 16 * ch * G::ROWB;
+                const int off1 = off0 + 8 * G::ROWB;
+                const i16x4_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(vs + off0));
+                const i16x4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(vs + off1));
+                const uint2 u0 = __builtin_bit_cast(uint2, t0), u1 = __builtin_bit_cast(uint2, t1);
+                const bf16x8_t va = __builtin_bit_cast(bf16x8_t, make_uint4(u0.x, u0.y, u1.x, u1.y));
+                acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[ch], acc_o[db], 0, 0, 0);
             }
         }
+        // Two transpose reads feed each MFMA; keep them PF MFMAs ahead.
+        constexpr int NM = (kBN / 16) * G::DB, PF = 4;
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF, 0);
+#pragma unroll
+        for (int i = 0; i < NM - PF; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, PF, 0);
+    };
 
-        if (j + 1 < n_tiles) stage_store((j + 1) & 1, m0 + kBN);
-        __syncthreads();
+    // Matrix phase of period j: PV(j-1), QK(j).
+    auto matrix_phase = [&](int j) __attribute__((always_inline)) {
+        if (j >= 1 && j - 1 < wave_tiles) pv(vslot(j - 1));
+        if (j < wave_tiles) qk(kslot(j), j * kBN);
+    };
+    // Loads issued at the start of a wave's matrix phase in period j: direct
+    // copies of V(j+1) and (no RoPE) K(j+2); with RoPE, the registers for the
+    // group's share of K(j+1) (A) or K(j+2) (B), stored in its next vector phase.
+    auto issue_loads = [&](int j) __attribute__((always_inline)) {
+        if constexpr (ROPE) {
+            const int t = j + 1 + grp;
+            if (t < T) rload_k(t * kBN, k_unit, k_key, k_pg);
+        }
+        if (j + 1 < T) dload_v(j + 1);
+        if constexpr (!ROPE) {
+            if (j + 2 < T) dload_k(j + 2);
+        }
+    };
+    // Before barrier Y(j): every load issued in period j-1 has landed.  The
+    // loads still allowed in flight are the ones issued in period j (loads
+    // retire in issue order).
+    auto wait_before_y = [&](int j) __attribute__((always_inline)) {
+        if constexpr (ROPE && WINDOW) {
+            wait_vmcnt<0>();  // pruned pair groups make the per-wave load count data dependent
+        } else if constexpr (ROPE) {
+            constexpr int RL = 4;  // K lo/hi and the cos/sin quarters of one unit
+            const bool rl = (j + 1 + grp < T) && (G::K_UNITS > 256 * grp);
+            if (j + 1 < T) {
+                if (rl) wait_vmcnt<RL + G::NI_W>();
+                else wait_vmcnt<G::NI_W>();
+            } else {
+                if (rl) wait_vmcnt<RL>();
+                else wait_vmcnt<0>();
+            }
+        } else {
+            if (j + 2 < T) wait_vmcnt<2 * G::NI_W>();
+            else if (j + 1 < T) wait_vmcnt<G::NI_W>();
+            else wait_vmcnt<0>();
+        }
+    };
+    auto vector_phase = [&](int ts, int tk) __attribute__((always_inline)) {
+        if (ts >= 0 && ts < wave_tiles) softmax(ts * kBN);
+        if constexpr (ROPE) {
+            if (tk < T) rstore_k(kslot(tk), tk * kBN, k_unit, k_key, k_pg);
+        }
+    };
+
+    // Prologue: K(0) (and, without RoPE, K(1)) and V(0) in LDS before Y(-1).
+    if (T > 0) {
+        if constexpr (ROPE) {
+            rload_k(0, tid, tid / G::PG, tid % G::PG);
+            rstore_k(kslot(0), 0, tid, tid / G::PG, tid % G::PG);
+        } else {
+            dload_k(0);
+            if (T > 1) dload_k(1);
+        }
+        dload_v(0);
+    }
+    wait_vmcnt<0>();
+    if constexpr (ROPE) {
+        if (grp == 1 && 1 < T) rload_k(kBN, k_unit, k_key, k_pg);  // B's share of K(1)
+    }
+    __syncthreads();  // Y(-1)
+
+    if (grp == 0) {
+        for (int j = 0; j <= T; ++j) {
+            issue_loads(j);
+            matrix_phase(j);
+            __syncthreads();  // X(j)
+            vector_phase(j, j + 1);
+            wait_before_y(j);
+            __syncthreads();  // Y(j)
+        }
+    } else {
+        for (int j = 0; j <= T; ++j) {
+            vector_phase(j - 1, j + 1);
+            __syncthreads();  // X(j)
+            issue_loads(j);
+            matrix_phase(j);
+            wait_before_y(j);
+            __syncthreads();  // Y(j)
+        }
     }
 
     // ---- epilogue: O / l, bf16, store --------------------------------------

@@ -11,13 +11,14 @@ namespace attn {
 // arguments is sized for it.
 constexpr int kMaxPairs = 64;
 
-// RoPE cos/sin table, fp32, built once per (device, D, theta) on the host in
-// fp64: for position p and pair group g (pairs 8g .. 8g+7) sixteen floats,
-// cos of the eight angles then sin of the eight angles.  A thread that
-// rotates one 8-pair group of one row reads these 64 contiguous bytes.
-// Index: ((p * (D / 16)) + g) * 16 + {0..7: cos, 8..15: sin}.
+// RoPE cos/sin table, built once per (device, D, theta) on the host in fp64
+// and stored rounded to fp16 (nearest even).  Position p and pair group g
+// (pairs 8g .. 8g+7) own two 16-byte quarters: the eight cosines, then the
+// eight sines.  Quarter i of (p, g) starts at half index
+// ((p * 2 + i) * (D / 16) + g) * 8, so the threads of one row that each
+// rotate one pair group read one contiguous run per quarter.
 struct RopeTable {
-    const float *cs = nullptr;
+    const uint16_t *cs = nullptr;
     int capacity = 0;  // number of positions held
 };
 
@@ -26,7 +27,7 @@ struct FwdArgs {
     const uint16_t *k;
     const uint16_t *v;
     uint16_t *o;
-    const float *rope_cs;  // null when RoPE is off
+    const uint16_t *rope_cs;  // fp16 cos/sin table; null when RoPE is off
     int B, Hq, Hkv, S, D;
     int causal;
     int use_window;
@@ -39,7 +40,7 @@ struct RopeArgs {
     const uint16_t *k;
     uint16_t *q_out;
     uint16_t *k_out;
-    const float *rope_cs;
+    const uint16_t *rope_cs;
     int B, Hq, Hkv, S, D;
 };
 
@@ -65,19 +66,25 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
 }
 
 // Rotate eight NeoX pairs held as two 16-byte groups: lo = dims 8g..8g+7 and
-// hi = dims D/2+8g..D/2+8g+7 of one row, with cs the 16 table floats of that
-// (position, group).  x' = x cos - y sin, y' = y cos + x sin, evaluated with
-// explicit fused multiply-adds so every caller rounds identically.
-__device__ __forceinline__ void rope_rotate8(uint4 &lo, uint4 &hi, const float *cs)
+// hi = dims D/2+8g..D/2+8g+7 of one row, with cq / sq the eight fp16 cosines
+// and sines of that (position, group).  x' = x cos - y sin,
+// y' = y cos + x sin in fp32 (fp16 -> fp32 is exact), evaluated with explicit
+// fused multiply-adds so every caller rounds identically.
+__device__ __forceinline__ float half_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)); }
+__device__ __forceinline__ float half_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+
+__device__ __forceinline__ void rope_rotate8(uint4 &lo, uint4 &hi, const uint4 cq, const uint4 sq)
 {
     uint32_t l[4] = {lo.x, lo.y, lo.z, lo.w};
     uint32_t h[4] = {hi.x, hi.y, hi.z, hi.w};
+    const uint32_t cw[4] = {cq.x, cq.y, cq.z, cq.w};
+    const uint32_t sw[4] = {sq.x, sq.y, sq.z, sq.w};
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
         float x0 = bf16_lo(l[w]), x1 = bf16_hi(l[w]);
         float y0 = bf16_lo(h[w]), y1 = bf16_hi(h[w]);
-        float c0 = cs[2 * w], c1 = cs[2 * w + 1];
-        float s0 = cs[8 + 2 * w], s1 = cs[8 + 2 * w + 1];
+        float c0 = half_lo(cw[w]), c1 = half_hi(cw[w]);
+        float s0 = half_lo(sw[w]), s1 = half_hi(sw[w]);
         float xr0 = __builtin_fmaf(x0, c0, -(y0 * s0));
         float xr1 = __builtin_fmaf(x1, c1, -(y1 * s1));
         float yr0 = __builtin_fmaf(y0, c0, x0 * s0);

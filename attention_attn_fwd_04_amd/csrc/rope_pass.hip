@@ -3,7 +3,7 @@
 // attention on the rotated copies).
 //
 // Memory-bound elementwise work: each thread rotates one 8-pair group of one
-// row (reads 2 x 16 bytes of the row and the 64-byte cos/sin entry of its
+// row (reads 2 x 16 bytes of the row and the two 16-byte cos/sin quarters of its
 // position, writes 2 x 16 bytes), using the same rotation routine and table
 // as the fused kernel so both produce identical bf16 bits.  Rows of Q and of
 // K are numbered together, Q rows first; a row is (b, s, h) in BSHD order, so
@@ -37,14 +37,9 @@ __global__ __launch_bounds__(kThreads) void rope_pass_kernel(const RopeArgs a, l
 
     uint4 lo = *reinterpret_cast<const uint4 *>(src + 8 * pg);
     uint4 hi = *reinterpret_cast<const uint4 *>(src + D / 2 + 8 * pg);
-    const float4 *cp = reinterpret_cast<const float4 *>(a.rope_cs + ((size_t)s * PG + pg) * 16);
-    float cs[16];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        float4 t = cp[i];
-        cs[4 * i] = t.x; cs[4 * i + 1] = t.y; cs[4 * i + 2] = t.z; cs[4 * i + 3] = t.w;
-    }
-    rope_rotate8(lo, hi, cs);
+    const uint4 cq = *reinterpret_cast<const uint4 *>(a.rope_cs + (((size_t)s * 2 + 0) * PG + pg) * 8);
+    const uint4 sq = *reinterpret_cast<const uint4 *>(a.rope_cs + (((size_t)s * 2 + 1) * PG + pg) * 8);
+    rope_rotate8(lo, hi, cq, sq);
     *reinterpret_cast<uint4 *>(dst + 8 * pg) = lo;
     *reinterpret_cast<uint4 *>(dst + D / 2 + 8 * pg) = hi;
 }
