@@ -27,23 +27,35 @@
 //    the contraction axis leaves Q'K'^T unchanged; this one keeps the two
 //    halves of a NeoX pair in the same MFMA, which the per-pair window uses.
 //  * A work-group of 8 waves (two per SIMD) owns 256 query rows, 32 per
-//    wave.  Each K/V tile staged in LDS is rotated once for 256 rows; while
-//    one wave of a SIMD runs its softmax the other can issue MFMAs.
-//  * K is rotated in registers while it is staged into LDS (each thread
-//    loads both halves of its pairs, so no half swap is needed).
+//    wave, and walks the key tiles in lock step, one barrier per tile.  Each
+//    wave software-pipelines its own work: the scores of tile i are computed
+//    by MFMAs while the same wave's VALU turns tile i-1's scores into P, and
+//    the PV MFMAs of tile i-1 run while the VALU rotates part of tile i+1.
+//    On gfx950 VALU work overlaps MFMAs well inside one wave's instruction
+//    stream (a few VALU operations and one or two exp per 32x32x16 MFMA come
+//    for free), and poorly when one wave only issues MFMAs while the other
+//    wave on the SIMD only issues VALU.
+//  * K, V (and with RoPE the cos/sin rows of each key tile) stream into LDS
+//    rings through buffer loads that write LDS directly (no registers).  With
+//    RoPE each K tile is then rotated in place, once for all 256 rows, each
+//    thread rotating one (key, 8-pair group) unit.
 //  * All global loads are buffer loads: rows past the sequence end read as
-//    zero, so staging has no lane-divergent branches and the loads of tile
-//    j+1 stay in flight while tile j is computed.
-//  * LDS tiles are XOR-swizzled in 16-byte chunks so the MFMA operand reads
-//    and the transpose reads are free of bank conflicts without padding.
-//  * The softmax rescale is lazy: the reference max only moves (and O, l are
-//    rescaled) when a row's max grows by more than 8 in log2 units, so P is
-//    at most 2^8 and the common tile skips the 64 multiplies of O.
+//    zero, so staging has no lane-divergent branches.
+//  * LDS tiles are XOR-swizzled in 16-byte chunks so the MFMA operand reads,
+//    the transpose reads and the rotation's reads and writes are free of bank
+//    conflicts without padding.
+//  * The softmax rescale is lazy: P is computed against the running reference
+//    max m_ref; only when a lane's partial row sum of P exceeds 2^14 (or is
+//    not finite: the first tile) is the tile's true max taken, O and l
+//    rescaled, and P recomputed.  So every P is at most 2^14, the common tile
+//    needs no max pass, and the 64 multiplies of O are rare.
 //  * Key tiles are visited from 0 upwards; the masked tiles are the last
 //    ones.  Query tiles are issued longest first, and the block index is
 //    remapped so one head's tiles run on one XCD (shared L2 for its K/V).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "attn_internal.h"
 
@@ -54,36 +66,47 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4_t;
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8_t;
+typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
+
+// 32-bit LDS address <-> LDS pointer.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) { return (uint32_t)(uintptr_t)(const lds_u8_t *)p; }
+__device__ __forceinline__ const lds_u8_t *lds_ptr(uint32_t a) { return (const lds_u8_t *)(uintptr_t)a; }
 
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kRowsPerWave = 32;
 constexpr int kBM = kWaves * kRowsPerWave;  // 256 query rows per work-group
 constexpr int kBN = 64;                     // keys per iteration (two 32-key blocks)
-constexpr float kRescaleLog2 = 8.0f;        // lazy-rescale threshold (P <= 2^8)
+constexpr float kLazyMaxSum = 16384.0f;     // lazy rescale: partial row sums of P stay <= 2^14
 
-template <int D>
+template <int D, bool ROPE>
 struct Geo {
     static constexpr int KCH = D / 16;      // MFMA k-steps over D (8 pairs each)
     static constexpr int PG = D / 16;       // 8-pair groups per row
     static constexpr int DB = D / 32;       // 32-row blocks of O^T
     static constexpr int CH = D / 8;        // 16-byte chunks per row
-    static constexpr int ROWB = D * 2;      // bytes per K / V row in LDS (unpadded)
-    static constexpr int TILE_B = kBN * ROWB;             // one K or V tile
+    static constexpr int ROWB = D * 2;      // bytes per K / V / cos-sin row in LDS (unpadded)
+    static constexpr int TILE_B = kBN * ROWB;             // one K, V or cos/sin tile
     static constexpr int NI = TILE_B / 1024;              // 1 KB direct-load instructions per tile
     static constexpr int NI_W = NI / kWaves;               // ... per wave
     static constexpr int RPI = 1024 / ROWB;               // rows per direct-load instruction
-    static constexpr int KRING = 0, VRING = 3 * TILE_B;   // 3-slot rings for K and V
-    static constexpr int RING_BYTES = 6 * TILE_B;
+    // Rings: K tile t in slot t % 4, V and cos/sin tiles in slot t % 3.
+    static constexpr int KSLOTS = 4, VSLOTS = 3, CSLOTS = 3;
+    static constexpr int KRING = 0;
+    static constexpr int VRING = KSLOTS * TILE_B;
+    static constexpr int CRING = VRING + VSLOTS * TILE_B;
+    static constexpr int RING_BYTES = CRING + (ROPE ? CSLOTS * TILE_B : 0);
     static constexpr int QP_B = ROWB + 16;                // padded Q staging rows
     static constexpr int Q_BYTES = kBM * QP_B;
     static constexpr int LDS_BYTES = (RING_BYTES > Q_BYTES) ? RING_BYTES : Q_BYTES;
     static constexpr int K_UNITS = kBN * PG;              // (key, pair group) rotation units
     static_assert(NI % kWaves == 0, "direct-load instructions split over the waves");
+    static_assert(LDS_BYTES <= 160 * 1024, "gfx950 LDS per work-group");
 
-    // K tiles are stored as rows of ROWB bytes whose 16-byte chunks are
-    // XOR-permuted per row: 16 lanes reading one logical chunk of 16
-    // consecutive rows hit 16 distinct 4-bank groups.
+    // K (and cos/sin) tiles are stored as rows of ROWB bytes whose 16-byte
+    // chunks are XOR-permuted per row: 16 lanes reading one logical chunk of
+    // 16 consecutive rows hit 16 distinct 4-bank groups.
     static __device__ __forceinline__ int kx(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
     static __device__ __forceinline__ int k_off(int r, int c) { return r * ROWB + ((c ^ kx(r)) << 4); }
     // V tiles: the 4 rows x 64 bytes half a wave of ds_read_b64_tr_b16 reads
@@ -213,7 +236,7 @@ __device__ __forceinline__ void window_chunk(const FwdArgs &a, bf16x8_t ka, bf16
 template <int D, bool ROPE, bool CAUSAL, bool WINDOW>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
 {
-    using G = Geo<D>;
+    using G = Geo<D, ROPE>;
     __shared__ __attribute__((aligned(16))) uint8_t smem[G::LDS_BYTES];
 
     const int tid = threadIdx.x;
@@ -246,7 +269,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
     const __amdgpu_buffer_rsrc_t q_rs = make_rsrc(a.q + ((size_t)b * S * a.Hq + hq) * D, (uint32_t)S * q_rowb);
     const __amdgpu_buffer_rsrc_t k_rs = make_rsrc(a.k + ((size_t)b * S * a.Hkv + hk) * D, (uint32_t)S * kv_rowb);
     const __amdgpu_buffer_rsrc_t v_rs = make_rsrc(a.v + ((size_t)b * S * a.Hkv + hk) * D, (uint32_t)S * kv_rowb);
-    const __amdgpu_buffer_rsrc_t cs_rs = make_rsrc(a.rope_cs, ROPE ? (uint32_t)S * G::PG * 32u : 0u);
+    const __amdgpu_buffer_rsrc_t cs_rs = make_rsrc(a.rope_cs, ROPE ? (uint32_t)S * G::ROWB : 0u);
     uint16_t *og = a.o + ((size_t)b * S * a.Hq + hq) * D;
 
     // ---- Q tile: load, rotate, stage through LDS into B-operand registers --
@@ -256,8 +279,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
         uint4 lo = bload16(q_rs, n * q_rowb + 16u * pg);
         uint4 hi = bload16(q_rs, n * q_rowb + (uint32_t)D + 16u * pg);
         if constexpr (ROPE) {
-            const uint4 cq = bload16(cs_rs, ((n * 2u + 0) * G::PG + pg) * 16u);
-            const uint4 sq = bload16(cs_rs, ((n * 2u + 1) * G::PG + pg) * 16u);
+            const uint4 cq = bload16(cs_rs, n * G::ROWB + 16u * pg);
+            const uint4 sq = bload16(cs_rs, n * G::ROWB + 16u * (G::PG + pg));
             rope_rotate8(lo, hi, cq, sq);
         }
         lds_at<uint4>(smem, row * G::QP_B + 16 * pg) = lo;
@@ -279,81 +302,65 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
     const int wave_tiles = wave_active ? (wave_kv_end + kBN - 1) / kBN : 0;
     const float c = a.scale_log2e;
 
-    // ---- ping-pong schedule ----------------------------------------------------
-    // The 8 waves form two groups, A = waves 0..3 and B = waves 4..7, one wave
-    // of each on every SIMD.  Each wave alternates a matrix phase (PV of the
-    // previous tile, then the scores of the current tile: 32 MFMAs) and a
-    // vector phase (mask, online softmax and P packing of the current tile,
-    // and, with RoPE, rotating its share of the next K tile into LDS).  Two
-    // barriers per period keep the groups half a period apart, so on every
-    // SIMD one wave's vector phase runs under the other wave's MFMAs:
-    //
-    //   period j:      [Y(j-1) .. X(j)]           [X(j) .. Y(j)]
-    //   group A:   PV(j-1), QK(j)              softmax(j)
-    //   group B:   softmax(j-1)                PV(j-1), QK(j)
-    //
-    // During period j only K(j) and V(j-1) are read.  K and V tiles live in
-    // 3-slot rings (tile t in slot t % 3).  V(j+1) and, without RoPE, K(j+2)
-    // are fetched with buffer loads straight into LDS during period j (each
-    // wave issues 1 KB per tile) and each wave waits for its own copies just
-    // before barrier Y(j+1); with RoPE, K(j+1) is loaded into registers,
-    // rotated and written during period j.
-    const int grp = wave >> 2;
-    auto kslot = [&](int t) __attribute__((always_inline)) { return smem + G::KRING + (t % 3) * G::TILE_B; };
+    // ---- schedule -----------------------------------------------------------
+    // Iteration i (all waves, i = 0 .. T) does, for this wave's rows:
+    //   block 1:  S(i) = K'(i) Q'^T (MFMA)  ||  rotate this thread's unit of K(i+1)
+    //   block 2:  O^T += V(i-1)^T P(i-1)^T  ||  P(i) = 2^(S(i) c - m c) (VALU)
+    // then one barrier.  Loads go straight into LDS: in iteration i, K(i+3)
+    // and its cos/sin rows (slot (i+3) % 4, % 3) and V(i+1) (slot (i+1) % 3).
+    // Each wave waits for its own loads of iteration i-1 before the barrier
+    // that ends iteration i, so K(t) is raw in LDS from the end of iteration
+    // t-2, rotated in t-1, read in t; V(t) is visible from iteration t+1 on.
+    auto kslot = [&](int t) __attribute__((always_inline)) { return smem + G::KRING + (t & 3) * G::TILE_B; };
     auto vslot = [&](int t) __attribute__((always_inline)) { return smem + G::VRING + (t % 3) * G::TILE_B; };
+    auto cslot = [&](int t) __attribute__((always_inline)) { return smem + G::CRING + (t % 3) * G::TILE_B; };
 
-    // Direct loads of this wave's share of a K or V tile: instructions
-    // wave + 8 i, each 1 KB = RPI rows; lane l writes chunk slot l % CH of row
-    // l / CH, i.e. the global chunk (slot ^ swizzle(row)).
+    // Direct loads of this wave's share of a tile: instructions wave + 8 i,
+    // each 1 KB = RPI rows; lane l writes chunk slot l % CH of row l / CH, i.e.
+    // the global chunk (slot ^ swizzle(row)).  Rows are keys (K, V) or
+    // positions (the cos/sin table, whose rows have the K row geometry).
     const int dl_row = lane / G::CH, dl_slot = lane % G::CH;
+    auto dload = [&](__amdgpu_buffer_rsrc_t rs, uint32_t rowb, uint8_t *dst, int t, bool vlayout)
+        __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < G::NI_W; ++i) {
+            const int ins = wave + kWaves * i;
+            const int r = ins * G::RPI + dl_row;
+            const int sw = vlayout ? G::vx(r) : G::kx(r);
+            const uint32_t off = (uint32_t)(t * kBN + r) * rowb + 16u * (uint32_t)(dl_slot ^ sw);
+            dma16(rs, off, dst + ins * 1024);
+        }
+    };
     auto dload_k = [&](int t) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < G::NI_W; ++i) {
-            const int ins = wave + kWaves * i;
-            const int r = ins * G::RPI + dl_row;
-            const uint32_t off = (uint32_t)(t * kBN + r) * kv_rowb + 16u * (uint32_t)(dl_slot ^ G::kx(r));
-            dma16(k_rs, off, kslot(t) + ins * 1024);
-        }
+        dload(k_rs, kv_rowb, kslot(t), t, false);
+        if constexpr (ROPE) dload(cs_rs, (uint32_t)G::ROWB, cslot(t), t, false);
     };
-    auto dload_v = [&](int t) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < G::NI_W; ++i) {
-            const int ins = wave + kWaves * i;
-            const int r = ins * G::RPI + dl_row;
-            const uint32_t off = (uint32_t)(t * kBN + r) * kv_rowb + 16u * (uint32_t)(dl_slot ^ (G::vx(r) >> 0));
-            dma16(v_rs, off, vslot(t) + ins * 1024);
-        }
-    };
+    auto dload_v = [&](int t) __attribute__((always_inline)) { dload(v_rs, kv_rowb, vslot(t), t, true); };
+    constexpr int LOADS_K = G::NI_W * (ROPE ? 2 : 1);   // per wave per K tile (with cos/sin)
+    constexpr int LOADS_V = G::NI_W;
 
-    // RoPE path: each group rotates half of the K tile (thread tg of the group
-    // owns unit tg + 256 grp: one key's 8-pair group).
-    const int tg = tid & 255;
-    const int k_unit = tg + 256 * grp;
-    const int k_key = k_unit / G::PG, k_pg = k_unit % G::PG;
-    uint4 k_lo = make_uint4(0, 0, 0, 0), k_hi = k_lo, k_cq = k_lo, k_sq = k_lo;
-
-    // Smallest query-key distance in the work-group's tile starting at key m0:
-    // a pair group whose widest window is below it is pruned everywhere in
-    // the tile, so its K columns are neither loaded nor rotated.
-    auto group_pruned = [&](int m0, int pg) __attribute__((always_inline)) {
-        const int dmin = max(0, n0 - (m0 + kBN - 1));
-        return WINDOW && a.window[8 * pg + 7] < dmin;
-    };
-    auto rload_k = [&](int m0, int unit, int key, int pg) __attribute__((always_inline)) {
-        if (unit < G::K_UNITS && !group_pruned(m0, pg)) {
-            const uint32_t m = (uint32_t)(m0 + key);
-            k_lo = bload16(k_rs, m * kv_rowb + 16u * pg);
-            k_hi = bload16(k_rs, m * kv_rowb + (uint32_t)D + 16u * pg);
-            k_cq = bload16(cs_rs, ((m * 2u + 0) * G::PG + pg) * 16u);
-            k_sq = bload16(cs_rs, ((m * 2u + 1) * G::PG + pg) * 16u);
-        }
-    };
-    auto rstore_k = [&](uint8_t *ks, int m0, int unit, int key, int pg) __attribute__((always_inline)) {
-        if (unit < G::K_UNITS && !group_pruned(m0, pg)) {  // pruned groups are never read
-            uint4 lo = k_lo, hi = k_hi;
-            rope_rotate8(lo, hi, k_cq, k_sq);
-            lds_at<uint4>(ks, G::k_off(key, pg)) = lo;
-            lds_at<uint4>(ks, G::k_off(key, G::PG + pg)) = hi;
+    // RoPE: thread tid rotates unit (key tid % 64, pair group tid / 64) of
+    // each K tile in place.  A pair group whose widest window is below the
+    // smallest query-key distance in the work-group's tile is pruned
+    // everywhere in it and is never read, so it is not rotated.
+    const int r_key = tid & (kBN - 1), r_pg = tid / kBN;
+    auto rotate_k = [&](int t) __attribute__((always_inline)) {
+        if constexpr (ROPE) {
+            if (tid < G::K_UNITS) {
+                if constexpr (WINDOW) {
+                    const int dmin = max(0, n0 - (t * kBN + kBN - 1));
+                    if (a.window[8 * r_pg + 7] < dmin) return;
+                }
+                uint8_t *ks = kslot(t);
+                const uint8_t *cs = cslot(t);
+                const int o_lo = G::k_off(r_key, r_pg), o_hi = G::k_off(r_key, G::PG + r_pg);
+                uint4 lo = lds_at<uint4>(ks, o_lo), hi = lds_at<uint4>(ks, o_hi);
+                const uint4 cq = lds_at<uint4>(const_cast<uint8_t *>(cs), o_lo);
+                const uint4 sq = lds_at<uint4>(const_cast<uint8_t *>(cs), o_hi);
+                rope_rotate8(lo, hi, cq, sq);
+                lds_at<uint4>(ks, o_lo) = lo;
+                lds_at<uint4>(ks, o_hi) = hi;
+            }
         }
     };
 
@@ -364,11 +371,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc_o[db][i] = 0.f;
     float m_ref = -__builtin_inff(), l_run = 0.f;
-    f32x16_t acc_s[2];
-    bf16x8_t pf[kBN / 16];
+    f32x16_t sc[2];                        // scores of one tile (S^T, two 32-key blocks)
+    bf16x8_t pf_a[kBN / 16], pf_b[kBN / 16];   // P of two consecutive tiles as PV B operands
 
-    // Per-lane LDS byte offsets of the MFMA operands; the tile base and the
-    // key-block / chunk terms are compile-time constants.
+    // Per-lane LDS byte offsets of the MFMA operands within a tile.
     // K operand of k-step kc: row l32 (+32 for the second key block), logical
     // chunk kc + PG g.
     int k_addr[G::KCH];
@@ -385,200 +391,328 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
     for (int db = 0; db < G::DB; ++db)
         v_addr[db] = G::v_off(4 * g + tr_key, (32 * db + tr_dim) >> 3) + 2 * (tr_dim & 4);
 
-    // S^T = K' Q'^T for the 64-key tile at m0 (two 32-key blocks).
-    auto qk = [&](const uint8_t *ks, int m0) __attribute__((always_inline)) {
+    // S^T = K' Q'^T for the 64-key tile t (two 32-key blocks).  The per-lane
+    // operand addresses are rebuilt per tile behind an empty asm so that the
+    // compiler folds the block offsets into the instructions' immediate
+    // offsets instead of keeping one precomputed address per read.
+    auto qk = [&](f32x16_t (&acc)[2], int t) __attribute__((always_inline)) {
+        const uint32_t kbase = lds_addr(kslot(t));
+        uint32_t kp[G::KCH];
+#pragma unroll
+        for (int kc = 0; kc < G::KCH; ++kc) {
+            kp[kc] = kbase + (uint32_t)k_addr[kc];
+            asm("" : "+v"(kp[kc]));
+        }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) acc_s[kb][i] = 0.f;
+            for (int i = 0; i < 16; ++i) acc[kb][i] = 0.f;
 #pragma unroll
         for (int kc = 0; kc < G::KCH; ++kc) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                const bf16x8_t ka = lds_at<bf16x8_t>(const_cast<uint8_t *>(ks), k_addr[kc] + kb * 32 * G::ROWB);
+                const bf16x8_t ka = *(const lds_bf16x8_t *)(lds_ptr(kp[kc]) + kb * 32 * G::ROWB);
                 if constexpr (WINDOW)
-                    window_chunk(a, ka, qreg[kc], acc_s[kb], kc, nw0, m0 + kb * 32, l32, g);
+                    window_chunk(a, ka, qreg[kc], acc[kb], kc, nw0, t * kBN + kb * 32, l32, g);
                 else
-                    acc_s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[kc], acc_s[kb], 0, 0, 0);
+                    acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[kc], acc[kb], 0, 0, 0);
             }
-        }
-        if constexpr (!WINDOW) {
-            // Keep the K operand reads PF steps ahead of the MFMAs that use
-            // them, so the LDS latency is hidden inside this wave.
-            constexpr int NM = 2 * G::KCH, PF = 4;
-            __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
-#pragma unroll
-            for (int i = 0; i < NM - PF; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, PF, 0);
         }
     };
 
-    // Mask, online-softmax update and bf16 packing of P for the tile at m0.
-    auto softmax = [&](int m0) __attribute__((always_inline)) {
-        const bool need_mask = (CAUSAL && m0 + kBN - 1 > nw0) || (m0 + kBN > S);
-        if (need_mask) {
-            const int n = nw0 + l32;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int m = m0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-                    const bool masked = (CAUSAL && m > n) || m >= S;
-                    acc_s[kb][i] = masked ? -__builtin_inff() : acc_s[kb][i];
-                }
-        }
-        float mx = acc_s[0][0];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, acc_s[kb][i]);
-        mx = max_halves(mx);
-        // Lazy rescale: move the reference max only when some row's max
-        // grew by more than 2^8 in probability; the decision is per wave.
-        const bool grow = (mx - m_ref) * c > kRescaleLog2;
-        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-            const float m_new = fmaxf(m_ref, mx);
-            const float alpha = fast_exp2((m_ref - m_new) * c);
-            l_run *= alpha;
-#pragma unroll
-            for (int db = 0; db < G::DB; ++db)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) acc_o[db][i] *= alpha;
-            m_ref = m_new;
-        }
-        const float mc = m_ref * c;
-        float rs = 0.f;
+    // Causal / sequence-end mask of tile t, needed only on the tiles that
+    // cross the wave's first row or the end of the sequence.
+    auto need_mask = [&](int t) __attribute__((always_inline)) {
+        const int m0 = t * kBN;
+        return (CAUSAL && m0 + kBN - 1 > nw0) || (m0 + kBN > S);
+    };
+    auto mask_tile = [&](f32x16_t (&s)[2], int t) __attribute__((always_inline)) {
+        const int m0 = t * kBN;
+        const int n = nw0 + l32;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const float p = fast_exp2(__builtin_fmaf(acc_s[kb][i], c, -mc));
-                acc_s[kb][i] = p;
-                rs += p;
+                const int m = m0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
+                const bool masked = (CAUSAL && m > n) || m >= S;
+                s[kb][i] = masked ? -__builtin_inff() : s[kb][i];
             }
-        l_run += rs;
+    };
+
+    // P = 2^(s c - m_ref c) of one (masked) tile, packed into pf; returns the
+    // lane's partial row sum.  m_ref = -inf gives inf / NaN sums, which force
+    // the exact path below.
+    auto exp_tile = [&](const f32x16_t (&s)[2], bf16x8_t (&pf)[kBN / 16]) __attribute__((always_inline)) {
+        const float nmc = -m_ref * c;
+        float r0 = 0.f, r1 = 0.f;
 #pragma unroll
         for (int ch = 0; ch < kBN / 16; ++ch) {
             const int kb = ch >> 1, h8 = (ch & 1) * 8;
+            float p[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) p[e] = fast_exp2(__builtin_fmaf(s[kb][h8 + e], c, nmc));
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                r0 += p[e];
+                r1 += p[e + 1];
+            }
             uint32_t w[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(acc_s[kb][h8 + 2 * e], acc_s[kb][h8 + 2 * e + 1]);
+            for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(p[2 * e], p[2 * e + 1]);
             pf[ch] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
         }
+        return r0 + r1;
+    };
+    // Exact path: move m_ref to the tile's row max, rescale O and l, redo P.
+    auto rescale_exp_tile = [&](const f32x16_t (&s)[2], bf16x8_t (&pf)[kBN / 16]) __attribute__((always_inline)) {
+        float mx = s[0][0];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+        mx = max_halves(mx);
+        const float m_new = fmaxf(m_ref, mx);
+        const float alpha = (m_new == m_ref) ? 1.0f : fast_exp2((m_ref - m_new) * c);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc_o[db][i] *= alpha;
+        m_ref = m_new;
+        return exp_tile(s, pf);
     };
 
-    // O^T += V^T P^T over four 16-key chunks of the V tile in vs.
-    auto pv = [&](const uint8_t *vs) __attribute__((always_inline)) {
+    // O^T += V^T P^T over the four 16-key chunks of V tile t.
+    auto pv = [&](int t, const bf16x8_t (&pf)[kBN / 16]) __attribute__((always_inline)) {
+        const uint32_t vbase = lds_addr(vslot(t));
+        uint32_t vp[G::DB];
+#pragma unroll
+        for (int db = 0; db < G::DB; ++db) {
+            vp[db] = vbase + (uint32_t)v_addr[db];
+            asm("" : "+v"(vp[db]));
+        }
 #pragma unroll
         for (int ch = 0; ch < kBN / 16; ++ch) {
 #pragma unroll
             for (int db = 0; db < G::DB; ++db) {
-                const int off0 = v_addr[db] + 16 * ch * G::ROWB;
-                const int off1 = off0 + 8 * G::ROWB;
-                const i16x4_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(vs + off0));
-                const i16x4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(vs + off1));
+                const lds_u8_t *p0 = lds_ptr(vp[db]) + 16 * ch * G::ROWB;
+                const i16x4_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)p0);
+                const i16x4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(p0 + 8 * G::ROWB));
                 const uint2 u0 = __builtin_bit_cast(uint2, t0), u1 = __builtin_bit_cast(uint2, t1);
                 const bf16x8_t va = __builtin_bit_cast(bf16x8_t, make_uint4(u0.x, u0.y, u1.x, u1.y));
                 acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[ch], acc_o[db], 0, 0, 0);
             }
         }
-        // Two transpose reads feed each MFMA; keep them PF MFMAs ahead.
-        constexpr int NM = (kBN / 16) * G::DB, PF = 4;
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF, 0);
+    };
+
+    // ---- the two steady-state blocks, hand-interleaved ---------------------
+    // Each block is a sequence of segments, one per MFMA, fenced with
+    // sched_barrier(0) so that the issue order is the one written here: the
+    // LDS reads of the MFMA PF segments ahead, the MFMA, then this segment's
+    // share of the VALU work.  The compiler still inserts the waits.
+    constexpr int NM1 = 2 * G::KCH;                 // QK MFMAs per tile
+    constexpr int NM2 = (kBN / 16) * G::DB;         // PV MFMAs per tile
+    constexpr int PF = 3;
+
+    // Block 1: S(i) = K'(i) Q'^T; with ROT, rotation of this thread's unit of
+    // K(i+1) spread over the MFMAs (one 32-bit word of each half at a time).
+    auto block1 = [&](auto rot_c, int i) __attribute__((always_inline)) {
+        constexpr bool ROT = decltype(rot_c)::value;
+        const uint32_t kbase = lds_addr(kslot(i));
+        uint32_t kp[G::KCH];
 #pragma unroll
-        for (int i = 0; i < NM - PF; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        for (int kc = 0; kc < G::KCH; ++kc) {
+            kp[kc] = kbase + (uint32_t)k_addr[kc];
+            asm("" : "+v"(kp[kc]));
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, PF, 0);
-    };
-
-    // Matrix phase of period j: PV(j-1), QK(j).
-    auto matrix_phase = [&](int j) __attribute__((always_inline)) {
-        if (j >= 1 && j - 1 < wave_tiles) pv(vslot(j - 1));
-        if (j < wave_tiles) qk(kslot(j), j * kBN);
-    };
-    // Loads issued at the start of a wave's matrix phase in period j: direct
-    // copies of V(j+1) and (no RoPE) K(j+2); with RoPE, the registers for the
-    // group's share of K(j+1) (A) or K(j+2) (B), stored in its next vector phase.
-    auto issue_loads = [&](int j) __attribute__((always_inline)) {
-        if constexpr (ROPE) {
-            const int t = j + 1 + grp;
-            if (t < T) rload_k(t * kBN, k_unit, k_key, k_pg);
+        bf16x8_t kop[NM1];
+        auto kread = [&](int k) __attribute__((always_inline)) {
+            kop[k] = *(const lds_bf16x8_t *)(lds_ptr(kp[k >> 1]) + (k & 1) * 32 * G::ROWB);
+        };
+        uint4 rlo, rhi, rcq, rsq;
+        uint8_t *rks = kslot(i + 1);
+        const int o_lo = G::k_off(r_key, r_pg), o_hi = G::k_off(r_key, G::PG + r_pg);
+        if constexpr (ROT) {
+            const uint8_t *rcs = cslot(i + 1);
+            rlo = lds_at<uint4>(rks, o_lo);
+            rhi = lds_at<uint4>(rks, o_hi);
+            rcq = lds_at<uint4>(const_cast<uint8_t *>(rcs), o_lo);
+            rsq = lds_at<uint4>(const_cast<uint8_t *>(rcs), o_hi);
         }
-        if (j + 1 < T) dload_v(j + 1);
-        if constexpr (!ROPE) {
-            if (j + 2 < T) dload_k(j + 2);
-        }
-    };
-    // Before barrier Y(j): every load issued in period j-1 has landed.  The
-    // loads still allowed in flight are the ones issued in period j (loads
-    // retire in issue order).
-    auto wait_before_y = [&](int j) __attribute__((always_inline)) {
-        if constexpr (ROPE && WINDOW) {
-            wait_vmcnt<0>();  // pruned pair groups make the per-wave load count data dependent
-        } else if constexpr (ROPE) {
-            constexpr int RL = 4;  // K lo/hi and the cos/sin quarters of one unit
-            const bool rl = (j + 1 + grp < T) && (G::K_UNITS > 256 * grp);
-            if (j + 1 < T) {
-                if (rl) wait_vmcnt<RL + G::NI_W>();
-                else wait_vmcnt<G::NI_W>();
-            } else {
-                if (rl) wait_vmcnt<RL>();
-                else wait_vmcnt<0>();
+#pragma unroll
+        for (int k = 0; k < PF; ++k) kread(k);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < NM1; ++k) {
+            if (k + PF < NM1) kread(k + PF);
+            const int kc = k >> 1, kb = k & 1;
+            if (kc == 0)
+                sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[k], qreg[kc], f32x16_t{}, 0, 0, 0);
+            else
+                sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[k], qreg[kc], sc[kb], 0, 0, 0);
+            if constexpr (ROT) {
+                constexpr int EVERY = NM1 / 4;
+                if (k % EVERY == EVERY - 1) {
+                    uint32_t &l = (k / EVERY == 0) ? rlo.x : (k / EVERY == 1) ? rlo.y : (k / EVERY == 2) ? rlo.z : rlo.w;
+                    uint32_t &h = (k / EVERY == 0) ? rhi.x : (k / EVERY == 1) ? rhi.y : (k / EVERY == 2) ? rhi.z : rhi.w;
+                    uint32_t cw = (k / EVERY == 0) ? rcq.x : (k / EVERY == 1) ? rcq.y : (k / EVERY == 2) ? rcq.z : rcq.w;
+                    uint32_t sw = (k / EVERY == 0) ? rsq.x : (k / EVERY == 1) ? rsq.y : (k / EVERY == 2) ? rsq.z : rsq.w;
+                    rope_rotate_word(l, h, cw, sw);
+                    asm volatile("" : "+v"(l), "+v"(h));
+                }
             }
-        } else {
-            if (j + 2 < T) wait_vmcnt<2 * G::NI_W>();
-            else if (j + 1 < T) wait_vmcnt<G::NI_W>();
-            else wait_vmcnt<0>();
+            __builtin_amdgcn_sched_barrier(0);
         }
-    };
-    auto vector_phase = [&](int ts, int tk) __attribute__((always_inline)) {
-        if (ts >= 0 && ts < wave_tiles) softmax(ts * kBN);
-        if constexpr (ROPE) {
-            if (tk < T) rstore_k(kslot(tk), tk * kBN, k_unit, k_key, k_pg);
+        if constexpr (ROT) {
+            lds_at<uint4>(rks, o_lo) = rlo;
+            lds_at<uint4>(rks, o_hi) = rhi;
         }
     };
 
-    // Prologue: K(0) (and, without RoPE, K(1)) and V(0) in LDS before Y(-1).
-    if (T > 0) {
-        if constexpr (ROPE) {
-            rload_k(0, tid, tid / G::PG, tid % G::PG);
-            rstore_k(kslot(0), 0, tid, tid / G::PG, tid % G::PG);
-        } else {
-            dload_k(0);
-            if (T > 1) dload_k(1);
+    // Block 2: O^T += V(i-1)^T P(i-1)^T from pp; with EXP, P(i) = 2^(S(i) c
+    // - m_ref c) into pn, two scores per step, 32 steps spread over the MFMAs.
+    // Returns the lane's partial row sum of P(i).
+    auto block2 = [&](auto exp_c, int i, const bf16x8_t (&pp)[kBN / 16], bf16x8_t (&pn)[kBN / 16])
+        __attribute__((always_inline)) {
+        constexpr bool EXP = decltype(exp_c)::value;
+        const uint32_t vbase = lds_addr(vslot(i - 1));
+        uint32_t vp[G::DB];
+#pragma unroll
+        for (int db = 0; db < G::DB; ++db) {
+            vp[db] = vbase + (uint32_t)v_addr[db];
+            asm("" : "+v"(vp[db]));
         }
-        dload_v(0);
-    }
+        i16x4_t vt0[NM2], vt1[NM2];
+        auto vread = [&](int k) __attribute__((always_inline)) {
+            const int ch = k / G::DB, db = k % G::DB;
+            const lds_u8_t *p0 = lds_ptr(vp[db]) + 16 * ch * G::ROWB;
+            vt0[k] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)p0);
+            vt1[k] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(p0 + 8 * G::ROWB));
+        };
+        const float nmc = -m_ref * c;
+        float r[4] = {0.f, 0.f, 0.f, 0.f};
+        uint32_t w[16];
+        // Step e: scores 2e, 2e+1 in P order (chunk e / 4, word e % 4).
+        // The empty volatile asm statement pins each step before the next
+        // fence (without it the arithmetic is sunk below the last MFMA).
+        auto exp_step = [&](int e) __attribute__((always_inline)) {
+            const int ch = e >> 2, kb = ch >> 1, h = (ch & 1) * 8 + 2 * (e & 3);
+            const float p0 = fast_exp2(__builtin_fmaf(sc[kb][h], c, nmc));
+            const float p1 = fast_exp2(__builtin_fmaf(sc[kb][h + 1], c, nmc));
+            r[e & 3] += p0 + p1;
+            w[e] = pack_bf16x2(p0, p1);
+            asm volatile("" : "+v"(w[e]), "+v"(r[e & 3]));
+        };
+#pragma unroll
+        for (int k = 0; k < PF; ++k) vread(k);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < NM2; ++k) {
+            if (k + PF < NM2) vread(k + PF);
+            const int ch = k / G::DB, db = k % G::DB;
+            const uint2 u0 = __builtin_bit_cast(uint2, vt0[k]), u1 = __builtin_bit_cast(uint2, vt1[k]);
+            const bf16x8_t va = __builtin_bit_cast(bf16x8_t, make_uint4(u0.x, u0.y, u1.x, u1.y));
+            acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pp[ch], acc_o[db], 0, 0, 0);
+            if constexpr (EXP) {
+                constexpr int PER = 16 / NM2;   // exp steps per MFMA
+#pragma unroll
+                for (int q = 0; q < PER; ++q) exp_step(k * PER + q);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (EXP) {
+#pragma unroll
+            for (int ch = 0; ch < kBN / 16; ++ch)
+                pn[ch] = __builtin_bit_cast(bf16x8_t, make_uint4(w[4 * ch], w[4 * ch + 1], w[4 * ch + 2], w[4 * ch + 3]));
+        }
+        return (r[0] + r[1]) + (r[2] + r[3]);
+    };
+
+    // ---- iterations ---------------------------------------------------------
+    // Iteration i issues its loads first and ends with the wait for the loads
+    // of iteration i-1 and the barrier; every wave runs all T + 1 iterations.
+    auto issue = [&](int i) __attribute__((always_inline)) {
+        if (i + 1 < T) dload_v(i + 1);
+        if (i + 3 < T) dload_k(i + 3);
+    };
+    auto finish = [&](int i) __attribute__((always_inline)) {
+        // Loads of iteration i-1 have landed; those of iteration i may fly.
+        if (i + 3 < T) wait_vmcnt<LOADS_V + LOADS_K>();
+        else if (i + 1 < T) wait_vmcnt<LOADS_V>();
+        else wait_vmcnt<0>();
+        __syncthreads();
+    };
+    // D = 64 has 256 rotation units: only waves 0..3 rotate (wave-uniform).
+    auto rot_on = [&](int i) __attribute__((always_inline)) { return ROPE && i + 1 < T && wave * 64 < G::K_UNITS; };
+    // S(i) into sc, with K(i+1) rotated alongside.
+    auto scores = [&](int i) __attribute__((always_inline)) {
+        if constexpr (WINDOW) {
+            qk(sc, i);
+            if (rot_on(i)) rotate_k(i + 1);
+        } else {
+            if (rot_on(i)) block1(std::true_type{}, i);
+            else block1(std::false_type{}, i);
+        }
+        if (need_mask(i)) mask_tile(sc, i);
+    };
+    auto accept = [&](float rs, bf16x8_t (&pn)[kBN / 16]) __attribute__((always_inline)) {
+        if (__builtin_amdgcn_ballot_w64(!(rs <= kLazyMaxSum)) != 0) rs = rescale_exp_tile(sc, pn);
+        l_run += rs;
+    };
+    // Steady state, 1 <= i < wave_tiles: S(i) || rotation; PV(i-1) from pp || P(i) into pn.
+    auto steady = [&](int i, const bf16x8_t (&pp)[kBN / 16], bf16x8_t (&pn)[kBN / 16]) __attribute__((always_inline)) {
+        issue(i);
+        scores(i);
+        accept(block2(std::true_type{}, i, pp, pn), pn);
+        finish(i);
+    };
+    // i = wave_tiles: the last PV; later iterations only load and rotate.
+    auto last_pv = [&](int i, const bf16x8_t (&pp)[kBN / 16], bf16x8_t (&scratch_pf)[kBN / 16]) __attribute__((always_inline)) {
+        issue(i);
+        if (rot_on(i)) rotate_k(i + 1);
+        block2(std::false_type{}, i, pp, scratch_pf);
+        finish(i);
+    };
+    auto idle = [&](int i) __attribute__((always_inline)) {
+        issue(i);
+        if (rot_on(i)) rotate_k(i + 1);
+        finish(i);
+    };
+
+    // Prologue: K(0..2) (with cos/sin) and V(0) in LDS, K(0) rotated.
+    dload_k(0);
+    if (1 < T) dload_k(1);
+    if (2 < T) dload_k(2);
+    dload_v(0);
     wait_vmcnt<0>();
+    __syncthreads();
     if constexpr (ROPE) {
-        if (grp == 1 && 1 < T) rload_k(kBN, k_unit, k_key, k_pg);  // B's share of K(1)
+        rotate_k(0);
+        __syncthreads();
     }
-    __syncthreads();  // Y(-1)
 
-    if (grp == 0) {
-        for (int j = 0; j <= T; ++j) {
-            issue_loads(j);
-            matrix_phase(j);
-            __syncthreads();  // X(j)
-            vector_phase(j, j + 1);
-            wait_before_y(j);
-            __syncthreads();  // Y(j)
+    int i = 0;
+    if (wave_tiles > 0) {
+        // iteration 0: S(0), P(0) into pf_a
+        issue(0);
+        scores(0);
+        accept(exp_tile(sc, pf_a), pf_a);
+        finish(0);
+        // P(j) is in pf_a for even j, in pf_b for odd j.
+        for (i = 1; i + 1 < wave_tiles; i += 2) {
+            steady(i, pf_a, pf_b);
+            steady(i + 1, pf_b, pf_a);
         }
-    } else {
-        for (int j = 0; j <= T; ++j) {
-            vector_phase(j - 1, j + 1);
-            __syncthreads();  // X(j)
-            issue_loads(j);
-            matrix_phase(j);
-            wait_before_y(j);
-            __syncthreads();  // Y(j)
+        if (i < wave_tiles) {
+            steady(i, pf_a, pf_b);
+            ++i;
+            last_pv(i, pf_b, pf_a);
+        } else {
+            last_pv(i, pf_a, pf_b);
         }
+        ++i;
     }
+    for (; i <= T; ++i) idle(i);
 
     // ---- epilogue: O / l, bf16, store --------------------------------------
     if (!wave_active) return;

@@ -73,27 +73,27 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
 __device__ __forceinline__ float half_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)); }
 __device__ __forceinline__ float half_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
 
+// One 32-bit word of each half: two pairs.
+__device__ __forceinline__ void rope_rotate_word(uint32_t &l, uint32_t &h, const uint32_t cw, const uint32_t sw)
+{
+    const float x0 = bf16_lo(l), x1 = bf16_hi(l);
+    const float y0 = bf16_lo(h), y1 = bf16_hi(h);
+    const float c0 = half_lo(cw), c1 = half_hi(cw);
+    const float s0 = half_lo(sw), s1 = half_hi(sw);
+    const float xr0 = __builtin_fmaf(x0, c0, -(y0 * s0));
+    const float xr1 = __builtin_fmaf(x1, c1, -(y1 * s1));
+    const float yr0 = __builtin_fmaf(y0, c0, x0 * s0);
+    const float yr1 = __builtin_fmaf(y1, c1, x1 * s1);
+    l = pack_bf16x2(xr0, xr1);
+    h = pack_bf16x2(yr0, yr1);
+}
+
 __device__ __forceinline__ void rope_rotate8(uint4 &lo, uint4 &hi, const uint4 cq, const uint4 sq)
 {
-    uint32_t l[4] = {lo.x, lo.y, lo.z, lo.w};
-    uint32_t h[4] = {hi.x, hi.y, hi.z, hi.w};
-    const uint32_t cw[4] = {cq.x, cq.y, cq.z, cq.w};
-    const uint32_t sw[4] = {sq.x, sq.y, sq.z, sq.w};
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        float x0 = bf16_lo(l[w]), x1 = bf16_hi(l[w]);
-        float y0 = bf16_lo(h[w]), y1 = bf16_hi(h[w]);
-        float c0 = half_lo(cw[w]), c1 = half_hi(cw[w]);
-        float s0 = half_lo(sw[w]), s1 = half_hi(sw[w]);
-        float xr0 = __builtin_fmaf(x0, c0, -(y0 * s0));
-        float xr1 = __builtin_fmaf(x1, c1, -(y1 * s1));
-        float yr0 = __builtin_fmaf(y0, c0, x0 * s0);
-        float yr1 = __builtin_fmaf(y1, c1, x1 * s1);
-        l[w] = pack_bf16x2(xr0, xr1);
-        h[w] = pack_bf16x2(yr0, yr1);
-    }
-    lo = make_uint4(l[0], l[1], l[2], l[3]);
-    hi = make_uint4(h[0], h[1], h[2], h[3]);
+    rope_rotate_word(lo.x, hi.x, cq.x, sq.x);
+    rope_rotate_word(lo.y, hi.y, cq.y, sq.y);
+    rope_rotate_word(lo.z, hi.z, cq.z, sq.z);
+    rope_rotate_word(lo.w, hi.w, cq.w, sq.w);
 }
 #endif
 
