@@ -132,6 +132,15 @@ __device__ __forceinline__ float sum_halves(float x)
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// acc + lo + hi of a packed pair of bf16 values (v_dot2_f32_bf16 against
+// (1, 1)).  The row sums l add up the bf16-rounded P that the PV MFMAs use.
+__device__ __forceinline__ float sum_bf16x2(uint32_t pair, float acc)
+{
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pair), bf16x2_t{(__bf16)1.0f, (__bf16)1.0f},
+                                           acc, false);
+}
+
 // Buffer resource over [base, base + bytes); loads beyond it return zero.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
 {
@@ -155,12 +164,36 @@ __device__ __forceinline__ T &lds_at(uint8_t *base, int off) { return *reinterpr
 // treat these asynchronous LDS writes as pending on every later LDS read and
 // barrier; the kernel waits for them itself (wait_vmcnt) before the barrier
 // that publishes the tile.  One wait state separates the M0 write from its use.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, const uint8_t *lds_base)
+// The same kind of buffer resource as four 32-bit words (base, stride 0,
+// size, flags), for the inline assembly below, which takes it as a scalar
+// operand.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4_t make_desc(const void *base, uint32_t bytes)
 {
-    const uint32_t m0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)lds_base;
+    const uint64_t p = (uint64_t)(uintptr_t)base;
+    u32x4_t d;
+    d.x = (uint32_t)p;
+    d.y = (uint32_t)(p >> 32) & 0xffffu;
+    d.z = bytes;
+    d.w = 0x00020000u;
+    return d;
+}
+
+__device__ __forceinline__ void dma16(u32x4_t r, uint32_t voff, const uint8_t *lds_base)
+{
+    // Both scalar operands pass through readfirstlane: free when the value
+    // already lives in SGPRs, one v_readfirstlane per word when register
+    // allocation moved it to a VGPR (the asm operands must be SGPRs).
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)lds_base);
+    u32x4_t rs;
+    rs.x = __builtin_amdgcn_readfirstlane(r.x);
+    rs.y = __builtin_amdgcn_readfirstlane(r.y);
+    rs.z = __builtin_amdgcn_readfirstlane(r.z);
+    rs.w = __builtin_amdgcn_readfirstlane(r.w);
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                  :
-                 : "v"(voff), "s"(r), "s"(m0)
+                 : "v"(voff), "s"(rs), "s"(m0)
                  : "memory", "m0");
 }
 
@@ -267,13 +300,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
     const uint32_t q_rowb = (uint32_t)a.Hq * D * 2;
     const uint32_t kv_rowb = (uint32_t)a.Hkv * D * 2;
     const __amdgpu_buffer_rsrc_t q_rs = make_rsrc(a.q + ((size_t)b * S * a.Hq + hq) * D, (uint32_t)S * q_rowb);
-    const __amdgpu_buffer_rsrc_t k_rs = make_rsrc(a.k + ((size_t)b * S * a.Hkv + hk) * D, (uint32_t)S * kv_rowb);
-    const __amdgpu_buffer_rsrc_t v_rs = make_rsrc(a.v + ((size_t)b * S * a.Hkv + hk) * D, (uint32_t)S * kv_rowb);
     const __amdgpu_buffer_rsrc_t cs_rs = make_rsrc(a.rope_cs, ROPE ? (uint32_t)S * G::ROWB : 0u);
+    // K, V and the cos/sin table for the direct-to-LDS loads.
+    const u32x4_t k_rs = make_desc(a.k + ((size_t)b * S * a.Hkv + hk) * D, (uint32_t)S * kv_rowb);
+    const u32x4_t v_rs = make_desc(a.v + ((size_t)b * S * a.Hkv + hk) * D, (uint32_t)S * kv_rowb);
+    const u32x4_t cs_desc = make_desc(a.rope_cs, ROPE ? (uint32_t)S * G::ROWB : 0u);
     uint16_t *og = a.o + ((size_t)b * S * a.Hq + hq) * D;
 
     // ---- Q tile: load, rotate, stage through LDS into B-operand registers --
-    for (int u = tid; u < kBM * G::PG; u += kThreads) {
+    static_assert((kBM * G::PG) % kThreads == 0, "whole Q staging rounds");
+#pragma unroll
+    for (int it = 0; it < kBM * G::PG / kThreads; ++it) {
+        const int u = tid + it * kThreads;
         const int row = u / G::PG, pg = u - row * G::PG;
         const uint32_t n = (uint32_t)(n0 + row);
         uint4 lo = bload16(q_rs, n * q_rowb + 16u * pg);
@@ -320,7 +358,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
     // the global chunk (slot ^ swizzle(row)).  Rows are keys (K, V) or
     // positions (the cos/sin table, whose rows have the K row geometry).
     const int dl_row = lane / G::CH, dl_slot = lane % G::CH;
-    auto dload = [&](__amdgpu_buffer_rsrc_t rs, uint32_t rowb, uint8_t *dst, int t, bool vlayout)
+    auto dload = [&](u32x4_t rs, uint32_t rowb, uint8_t *dst, int t, bool vlayout)
         __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < G::NI_W; ++i) {
@@ -333,20 +371,38 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
     };
     auto dload_k = [&](int t) __attribute__((always_inline)) {
         dload(k_rs, kv_rowb, kslot(t), t, false);
-        if constexpr (ROPE) dload(cs_rs, (uint32_t)G::ROWB, cslot(t), t, false);
+        if constexpr (ROPE) dload(cs_desc, (uint32_t)G::ROWB, cslot(t), t, false);
     };
     auto dload_v = [&](int t) __attribute__((always_inline)) { dload(v_rs, kv_rowb, vslot(t), t, true); };
-    constexpr int LOADS_K = G::NI_W * (ROPE ? 2 : 1);   // per wave per K tile (with cos/sin)
-    constexpr int LOADS_V = G::NI_W;
+    // Loads of iteration i, one 1 KB instruction per step: V(i+1), K(i+3)
+    // and, with RoPE, the cos/sin rows of K(i+3).  They are issued in every
+    // iteration: tiles past the end read as zeros into slots that are free
+    // and never read again, which keeps the wait counts constant.
+    constexpr int NDMA = G::NI_W * (ROPE ? 3 : 2);
+    auto dma_step = [&](int i, int j) __attribute__((always_inline)) {
+        const int which = j / G::NI_W, ins = wave + kWaves * (j % G::NI_W);
+        const int r = ins * G::RPI + dl_row;
+        if (which == 0) {
+            const uint32_t off = (uint32_t)((i + 1) * kBN + r) * kv_rowb + 16u * (uint32_t)(dl_slot ^ G::vx(r));
+            dma16(v_rs, off, vslot(i + 1) + ins * 1024);
+        } else if (which == 1) {
+            const uint32_t off = (uint32_t)((i + 3) * kBN + r) * kv_rowb + 16u * (uint32_t)(dl_slot ^ G::kx(r));
+            dma16(k_rs, off, kslot(i + 3) + ins * 1024);
+        } else {
+            const uint32_t off = (uint32_t)((i + 3) * kBN + r) * (uint32_t)G::ROWB + 16u * (uint32_t)(dl_slot ^ G::kx(r));
+            dma16(cs_desc, off, cslot(i + 3) + ins * 1024);
+        }
+    };
 
-    // RoPE: thread tid rotates unit (key tid % 64, pair group tid / 64) of
+    // RoPE: lane l of wave w rotates unit (key l, pair group w) of
     // each K tile in place.  A pair group whose widest window is below the
     // smallest query-key distance in the work-group's tile is pruned
     // everywhere in it and is never read, so it is not rotated.
-    const int r_key = tid & (kBN - 1), r_pg = tid / kBN;
+    static_assert(kBN == 64, "one rotation pair group per wave");
+    const int r_key = lane, r_pg = wave;
     auto rotate_k = [&](int t) __attribute__((always_inline)) {
         if constexpr (ROPE) {
-            if (tid < G::K_UNITS) {
+            if (wave * 64 < G::K_UNITS) {   // K_UNITS is a multiple of 64: wave-uniform
                 if constexpr (WINDOW) {
                     const int dmin = max(0, n0 - (t * kBN + kBN - 1));
                     if (a.window[8 * r_pg + 7] < dmin) return;
@@ -451,14 +507,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
             float p[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) p[e] = fast_exp2(__builtin_fmaf(s[kb][h8 + e], c, nmc));
-#pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-                r0 += p[e];
-                r1 += p[e + 1];
-            }
             uint32_t w[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(p[2 * e], p[2 * e + 1]);
+            r0 = sum_bf16x2(w[0], sum_bf16x2(w[2], r0));
+            r1 = sum_bf16x2(w[1], sum_bf16x2(w[3], r1));
             pf[ch] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
         }
         return r0 + r1;
@@ -545,6 +598,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
 #pragma unroll
         for (int k = 0; k < NM1; ++k) {
             if (k + PF < NM1) kread(k + PF);
+            {
+                constexpr int EVERY_DMA = (NM1 - 2) / NDMA;
+                if (k % EVERY_DMA == 1 && k / EVERY_DMA < NDMA) dma_step(i, k / EVERY_DMA);
+            }
             const int kc = k >> 1, kb = k & 1;
             if (kc == 0)
                 sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[k], qreg[kc], f32x16_t{}, 0, 0, 0);
@@ -599,8 +656,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
             const int ch = e >> 2, kb = ch >> 1, h = (ch & 1) * 8 + 2 * (e & 3);
             const float p0 = fast_exp2(__builtin_fmaf(sc[kb][h], c, nmc));
             const float p1 = fast_exp2(__builtin_fmaf(sc[kb][h + 1], c, nmc));
-            r[e & 3] += p0 + p1;
             w[e] = pack_bf16x2(p0, p1);
+            r[e & 3] = sum_bf16x2(w[e], r[e & 3]);
             asm volatile("" : "+v"(w[e]), "+v"(r[e & 3]));
         };
 #pragma unroll
@@ -632,21 +689,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
     // Iteration i issues its loads first and ends with the wait for the loads
     // of iteration i-1 and the barrier; every wave runs all T + 1 iterations.
     auto issue = [&](int i) __attribute__((always_inline)) {
-        if (i + 1 < T) dload_v(i + 1);
-        if (i + 3 < T) dload_k(i + 3);
+#pragma unroll
+        for (int j = 0; j < NDMA; ++j) dma_step(i, j);
     };
     auto finish = [&](int i) __attribute__((always_inline)) {
-        // Loads of iteration i-1 have landed; those of iteration i may fly.
-        if (i + 3 < T) wait_vmcnt<LOADS_V + LOADS_K>();
-        else if (i + 1 < T) wait_vmcnt<LOADS_V>();
-        else wait_vmcnt<0>();
+        wait_vmcnt<NDMA>();   // loads of iteration i-1 have landed; those of iteration i may fly
         __syncthreads();
     };
     // D = 64 has 256 rotation units: only waves 0..3 rotate (wave-uniform).
     auto rot_on = [&](int i) __attribute__((always_inline)) { return ROPE && i + 1 < T && wave * 64 < G::K_UNITS; };
     // S(i) into sc, with K(i+1) rotated alongside.
+    // Block 1 with S(i); also issues the loads of iteration i.
     auto scores = [&](int i) __attribute__((always_inline)) {
         if constexpr (WINDOW) {
+            issue(i);
             qk(sc, i);
             if (rot_on(i)) rotate_k(i + 1);
         } else {
@@ -661,8 +717,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
     };
     // Steady state, 1 <= i < wave_tiles: S(i) || rotation; PV(i-1) from pp || P(i) into pn.
     auto steady = [&](int i, const bf16x8_t (&pp)[kBN / 16], bf16x8_t (&pn)[kBN / 16]) __attribute__((always_inline)) {
-        issue(i);
-        scores(i);
+        scores(i);   // issues the loads of iteration i between its MFMAs
         accept(block2(std::true_type{}, i, pp, pn), pn);
         finish(i);
     };
@@ -694,7 +749,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
     int i = 0;
     if (wave_tiles > 0) {
         // iteration 0: S(0), P(0) into pf_a
-        issue(0);
         scores(0);
         accept(exp_tile(sc, pf_a), pf_a);
         finish(0);
@@ -713,6 +767,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
         ++i;
     }
     for (; i <= T; ++i) idle(i);
+    wait_vmcnt<0>();   // no load may still be writing LDS when the work-group ends
 
     // ---- epilogue: O / l, bf16, store --------------------------------------
     if (!wave_active) return;
