@@ -206,20 +206,8 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// ---------------------------------------------------------------------------
-// Per-pair distance window on one 32-key x 32-query block and one MFMA
-// k-step kc, which holds the 8 complete pairs r = 8 kc .. 8 kc + 7 ("ATFlash
-// -- Per-RoPE-Wavelength Attention Windows", "The idea": pair r contributes
-// to score (n, m) only when n - m <= w[r]; w is non-decreasing in r).  The
-// block's distances lie in [dlo, dhi] (dhi clipped to rows that are stored;
-// causally masked cells are discarded later, so dlo is clamped at 0).
-//  - every pair below dlo: the chunk is skipped (never multiplied);
-//  - every pair at or above dhi: the usual MFMA;
-//  - otherwise one MFMA over the pairs kept in the whole block (the others
-//    zeroed in the K operand), plus, for each pair whose limit falls inside
-//    [dlo, dhi), an MFMA of that pair alone added only where n - m <= w[r].
-// All decisions depend on block coordinates only: wave-uniform branches.
-// ---------------------------------------------------------------------------
+// Zero the pairs of an 8-pair K operand chunk whose bit in keep_bits is clear
+// (element e of the chunk belongs to pair e of the 8 in both lane halves).
 __device__ __forceinline__ bf16x8_t mask_pairs(bf16x8_t x, uint32_t keep_bits)
 {
     uint4 u = __builtin_bit_cast(uint4, x);
@@ -233,37 +221,35 @@ __device__ __forceinline__ bf16x8_t mask_pairs(bf16x8_t x, uint32_t keep_bits)
     return __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
 }
 
-__device__ __forceinline__ void window_chunk(const FwdArgs &a, bf16x8_t ka, bf16x8_t qop, f32x16_t &acc,
-                                             int kc, int nq0, int mk0, int l32, int g)
+// The same masks as a table in constant memory, for keep bits that are
+// wave-uniform: entry b holds the four operand-word masks of mask_pairs(., b),
+// fetched with one scalar load.
+struct alignas(16) PairMaskTable {
+    uint32_t w[256][4];
+};
+constexpr PairMaskTable make_pair_masks()
 {
-    const int dlo = max(0, nq0 - (mk0 + 31));
-    const int dhi = min(nq0 + 31, a.S - 1) - mk0;
-    const int r0 = 8 * kc;
-    if (a.window[r0 + 7] < dlo) return;  // all 8 pairs pruned in this block
-    if (a.window[r0] >= dhi) {           // all 8 pairs kept in this block
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qop, acc, 0, 0, 0);
-        return;
-    }
-    uint32_t keep = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-        if (a.window[r0 + j] >= dhi) keep |= 1u << j;
-    if (keep) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mask_pairs(ka, keep), qop, acc, 0, 0, 0);
-    const int n = nq0 + l32;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int w = a.window[r0 + j];
-        if (w < dlo || w >= dhi) continue;  // pruned or kept in the whole block
-        f32x16_t part;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) part[i] = 0.f;
-        part = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mask_pairs(ka, 1u << j), qop, part, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int m = mk0 + 8 * (i >> 2) + 4 * g + (i & 3);
-            acc[i] += (n - m <= w) ? part[i] : 0.0f;
-        }
-    }
+    PairMaskTable t{};
+    for (int b = 0; b < 256; ++b)
+        for (int i = 0; i < 4; ++i)
+            t.w[b][i] = (((b >> (2 * i)) & 1) ? 0x0000ffffu : 0u) | (((b >> (2 * i + 1)) & 1) ? 0xffff0000u : 0u);
+    return t;
+}
+__constant__ PairMaskTable kPairMasks = make_pair_masks();
+
+struct WordMask {
+    uint32_t m[4];
+};
+__device__ __forceinline__ WordMask pair_mask(uint64_t keep, int kc)
+{
+    const uint32_t b = (uint32_t)(keep >> (8 * kc)) & 0xffu;
+    const uint4 t = *reinterpret_cast<const uint4 *>(&kPairMasks.w[b][0]);
+    return WordMask{{t.x, t.y, t.z, t.w}};
+}
+__device__ __forceinline__ bf16x8_t apply_mask(bf16x8_t x, const WordMask &m)
+{
+    const uint4 u = __builtin_bit_cast(uint4, x);
+    return __builtin_bit_cast(bf16x8_t, make_uint4(u.x & m.m[0], u.y & m.m[1], u.z & m.m[2], u.w & m.m[3]));
 }
 
 template <int D, bool ROPE, bool CAUSAL, bool WINDOW>
@@ -339,6 +325,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
     const int wave_kv_end = CAUSAL ? min(S, nw0 + kRowsPerWave) : S;
     const int wave_tiles = wave_active ? (wave_kv_end + kBN - 1) / kBN : 0;
     const float c = a.scale_log2e;
+    // Per-pair window table, read in place in the kernel-argument segment (the
+    // kernel's only argument, at offset 0) so that runtime-indexed reads are
+    // scalar loads rather than reads of a private copy of the arguments.
+    typedef __attribute__((address_space(4))) const int32_t kconst_i32;
+    kconst_i32 *wtab = (kconst_i32 *)((__attribute__((address_space(4))) const char *)
+                                          __builtin_amdgcn_kernarg_segment_ptr() + __builtin_offsetof(FwdArgs, window));
 
     // ---- schedule -----------------------------------------------------------
     // Iteration i (all waves, i = 0 .. T) does, for this wave's rows:
@@ -400,12 +392,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
     // everywhere in it and is never read, so it is not rotated.
     static_assert(kBN == 64, "one rotation pair group per wave");
     const int r_key = lane, r_pg = wave;
+    const int w_rot = WINDOW ? wtab[8 * r_pg + 7] : 0;   // widest window of the pair group
     auto rotate_k = [&](int t) __attribute__((always_inline)) {
         if constexpr (ROPE) {
             if (wave * 64 < G::K_UNITS) {   // K_UNITS is a multiple of 64: wave-uniform
                 if constexpr (WINDOW) {
                     const int dmin = max(0, n0 - (t * kBN + kBN - 1));
-                    if (a.window[8 * r_pg + 7] < dmin) return;
+                    if (w_rot < dmin) return;
                 }
                 uint8_t *ks = kslot(t);
                 const uint8_t *cs = cslot(t);
@@ -446,35 +439,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
 #pragma unroll
     for (int db = 0; db < G::DB; ++db)
         v_addr[db] = G::v_off(4 * g + tr_key, (32 * db + tr_dim) >> 3) + 2 * (tr_dim & 4);
-
-    // S^T = K' Q'^T for the 64-key tile t (two 32-key blocks).  The per-lane
-    // operand addresses are rebuilt per tile behind an empty asm so that the
-    // compiler folds the block offsets into the instructions' immediate
-    // offsets instead of keeping one precomputed address per read.
-    auto qk = [&](f32x16_t (&acc)[2], int t) __attribute__((always_inline)) {
-        const uint32_t kbase = lds_addr(kslot(t));
-        uint32_t kp[G::KCH];
-#pragma unroll
-        for (int kc = 0; kc < G::KCH; ++kc) {
-            kp[kc] = kbase + (uint32_t)k_addr[kc];
-            asm("" : "+v"(kp[kc]));
-        }
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc[kb][i] = 0.f;
-#pragma unroll
-        for (int kc = 0; kc < G::KCH; ++kc) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const bf16x8_t ka = *(const lds_bf16x8_t *)(lds_ptr(kp[kc]) + kb * 32 * G::ROWB);
-                if constexpr (WINDOW)
-                    window_chunk(a, ka, qreg[kc], acc[kb], kc, nw0, t * kBN + kb * 32, l32, g);
-                else
-                    acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[kc], acc[kb], 0, 0, 0);
-            }
-        }
-    };
 
     // Causal / sequence-end mask of tile t, needed only on the tiles that
     // cross the wave's first row or the end of the sequence.
@@ -558,6 +522,36 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
         }
     };
 
+    // ---- per-pair window ("ATFlash -- Per-RoPE-Wavelength Attention Windows",
+    // "The idea": pair r contributes to score (n, m) only when n - m <= w[r]) --
+    // Lane r holds w[r] (pairs past D/2: never pruned).  Comparing it with a
+    // block's distance bounds and taking the ballot gives, in scalar
+    // registers, the pairs pruned on the whole block, the pairs kept on the
+    // whole block and, in between, the pairs whose limit falls inside it.
+    const int w_lane = (WINDOW && lane < D / 2) ? wtab[lane] : INT_MAX;
+    // The partial pairs of one 32-key block: each by an MFMA of that pair
+    // alone, counted only where n - m <= w[r].  Wave-uniform branches.
+    auto window_partial = [&](f32x16_t &acc, uint64_t bits, uint32_t kbase_blk, int m0) __attribute__((always_inline)) {
+        const int n = nw0 + l32;
+        while (bits) {
+            const int r = __builtin_ctzll(bits);
+            bits &= bits - 1;
+            const int kc = r >> 3, j = r & 7;
+            const int w = __builtin_amdgcn_readlane(w_lane, r);
+            const bf16x8_t ka = mask_pairs(*(const lds_bf16x8_t *)lds_ptr(kbase_blk + (uint32_t)G::k_off(l32, kc + G::PG * g)),
+                                           1u << j);
+            f32x16_t one{};
+#pragma unroll
+            for (int c2 = 0; c2 < G::KCH; ++c2)   // the Q operand register of chunk kc
+                if (kc == c2) one = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[c2], f32x16_t{}, 0, 0, 0);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int m = m0 + 8 * (e >> 2) + 4 * g + (e & 3);
+                acc[e] += (n - m <= w) ? one[e] : 0.0f;
+            }
+        }
+    };
+
     // ---- the two steady-state blocks, hand-interleaved ---------------------
     // Each block is a sequence of segments, one per MFMA, fenced with
     // sched_barrier(0) so that the issue order is the one written here: the
@@ -603,10 +597,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
                 if (k % EVERY_DMA == 1 && k / EVERY_DMA < NDMA) dma_step(i, k / EVERY_DMA);
             }
             const int kc = k >> 1, kb = k & 1;
-            if (kc == 0)
+            if (kc == 0) {
                 sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[k], qreg[kc], f32x16_t{}, 0, 0, 0);
-            else
+            } else {
                 sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[k], qreg[kc], sc[kb], 0, 0, 0);
+            }
             if constexpr (ROT) {
                 constexpr int EVERY = NM1 / 4;
                 if (k % EVERY == EVERY - 1) {
@@ -617,6 +612,83 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
                     rope_rotate_word(l, h, cw, sw);
                     asm volatile("" : "+v"(l), "+v"(h));
                 }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (ROT) {
+            lds_at<uint4>(rks, o_lo) = rlo;
+            lds_at<uint4>(rks, o_hi) = rhi;
+        }
+    };
+
+    // Block 1 with a window.  Per 32-key block, wprune / wkeep mark the pairs
+    // pruned / kept on the whole block.  The 8-pair chunks of a tile then fall
+    // into: chunks below NS, pruned on both blocks (no MFMA); chunks NS and
+    // NS + 1, computed over each block's kept pairs (masked operand); chunks
+    // from NS + 2 on, kept on both blocks (plain MFMA).  NS < 0: every chunk
+    // masked.  NS is a template constant, so each variant is a fixed sequence
+    // of MFMAs with this iteration's loads and rotation spread over it.
+    auto block1w = [&](auto rot_c, auto ns_c, int i, const uint64_t (&wprune)[2], const uint64_t (&wkeep)[2])
+        __attribute__((always_inline)) {
+        constexpr bool ROT = decltype(rot_c)::value;
+        constexpr int NS = decltype(ns_c)::value;
+        constexpr bool GEN = NS < 0;
+        constexpr int C0 = GEN ? 0 : NS;                  // first chunk computed
+        constexpr int NM = 2 * (G::KCH - C0);             // MFMAs of this variant
+        static_assert(NM >= 4, "rotation words spread over the MFMAs");
+        const uint32_t kbase = lds_addr(kslot(i));
+        uint32_t kp[G::KCH];
+#pragma unroll
+        for (int kc = 0; kc < G::KCH; ++kc) {
+            kp[kc] = kbase + (uint32_t)k_addr[kc];
+            asm("" : "+v"(kp[kc]));
+        }
+        bf16x8_t kop[NM];
+        auto kread = [&](int k) __attribute__((always_inline)) {
+            kop[k] = *(const lds_bf16x8_t *)(lds_ptr(kp[C0 + (k >> 1)]) + (k & 1) * 32 * G::ROWB);
+        };
+        uint4 rlo, rhi, rcq, rsq;
+        uint8_t *rks = kslot(i + 1);
+        const int o_lo = G::k_off(r_key, r_pg), o_hi = G::k_off(r_key, G::PG + r_pg);
+        if constexpr (ROT) {
+            const uint8_t *rcs = cslot(i + 1);
+            rlo = lds_at<uint4>(rks, o_lo);
+            rhi = lds_at<uint4>(rks, o_hi);
+            rcq = lds_at<uint4>(const_cast<uint8_t *>(rcs), o_lo);
+            rsq = lds_at<uint4>(const_cast<uint8_t *>(rcs), o_hi);
+        }
+        WordMask msk[2][2];   // chunks NS, NS + 1 of each block
+        if constexpr (!GEN) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) msk[kb][j] = pair_mask(wkeep[kb], NS + j);
+        }
+#pragma unroll
+        for (int k = 0; k < PF && k < NM; ++k) kread(k);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < NM; ++k) {
+            if (k + PF < NM) kread(k + PF);
+#pragma unroll
+            for (int j = 0; j < NDMA; ++j)
+                if (j * NM / NDMA == k) dma_step(i, j);
+            const int kc = C0 + (k >> 1), kb = k & 1;
+            bf16x8_t op = kop[k];
+            if constexpr (GEN) op = apply_mask(op, pair_mask(wkeep[kb], kc));
+            else if (kc < NS + 2) op = apply_mask(op, msk[kb][kc - NS]);
+            sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, qreg[kc], kc == C0 ? f32x16_t{} : sc[kb], 0, 0, 0);
+            if constexpr (ROT) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if ((r + 1) * NM / 4 - 1 == k) {
+                        uint32_t &l = (r == 0) ? rlo.x : (r == 1) ? rlo.y : (r == 2) ? rlo.z : rlo.w;
+                        uint32_t &h = (r == 0) ? rhi.x : (r == 1) ? rhi.y : (r == 2) ? rhi.z : rhi.w;
+                        const uint32_t cw = (r == 0) ? rcq.x : (r == 1) ? rcq.y : (r == 2) ? rcq.z : rcq.w;
+                        const uint32_t sw = (r == 0) ? rsq.x : (r == 1) ? rsq.y : (r == 2) ? rsq.z : rsq.w;
+                        rope_rotate_word(l, h, cw, sw);
+                        asm volatile("" : "+v"(l), "+v"(h));
+                    }
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -697,19 +769,69 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
         __syncthreads();
     };
     // D = 64 has 256 rotation units: only waves 0..3 rotate (wave-uniform).
-    auto rot_on = [&](int i) __attribute__((always_inline)) { return ROPE && i + 1 < T && wave * 64 < G::K_UNITS; };
+    // With a window, a pair group pruned on the whole work-group tile is
+    // never read, so it is not rotated.
+    auto rot_on = [&](int i) __attribute__((always_inline)) {
+        return ROPE && i + 1 < T && wave * 64 < G::K_UNITS &&
+               !(WINDOW && w_rot < max(0, n0 - ((i + 1) * kBN + kBN - 1)));
+    };
     // S(i) into sc, with K(i+1) rotated alongside.
     // Block 1 with S(i); also issues the loads of iteration i.
+    // With a window: the distances of this wave's 32 queries to the two
+    // 32-key blocks of tile i lie in [dlo, dhi] (dlo clamped at 0: causally
+    // masked cells are discarded later; dhi clipped to stored rows); the
+    // variant NS is the even number of leading chunks pruned on both blocks,
+    // valid if every chunk from NS + 2 on is kept on both (else the generic
+    // one).  VARIANTS false: the generic variant only.
+    auto scores_w = [&](auto variants_c, int i) __attribute__((always_inline)) {
+        uint64_t wprune[2], wkeep[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const int mk0 = i * kBN + kb * 32;
+            const int dlo = max(0, nw0 - (mk0 + 31)), dhi = min(nw0 + 31, S - 1) - mk0;
+            wprune[kb] = __builtin_amdgcn_ballot_w64(w_lane < dlo);
+            wkeep[kb] = ~__builtin_amdgcn_ballot_w64(w_lane < dhi);
+        }
+        int ns = -1;
+        if constexpr (decltype(variants_c)::value) {
+            const uint64_t pr = wprune[0] & wprune[1], kp = wkeep[0] & wkeep[1];
+            const int lead = (~pr == 0) ? 64 : __builtin_ctzll(~pr);
+            ns = min((lead >> 3) & ~1, G::KCH - 2);
+            const int top = 8 * (ns + 2);
+            if (top < 64 && (kp | ((1ull << top) - 1)) != ~0ull) ns = -1;
+        }
+        const bool rot = rot_on(i);
+        auto run = [&](auto ns_c) __attribute__((always_inline)) {
+            if (rot) block1w(std::true_type{}, ns_c, i, wprune, wkeep);
+            else block1w(std::false_type{}, ns_c, i, wprune, wkeep);
+        };
+        if constexpr (decltype(variants_c)::value) {
+            static_assert(G::KCH == 4 || G::KCH == 8, "variant list");
+            // (the partial pairs are added after the variant's MFMAs)
+            if (ns == 0) run(std::integral_constant<int, 0>{});
+            else if (ns == 2) run(std::integral_constant<int, 2>{});
+            else if (G::KCH == 8 && ns == 4) run(std::integral_constant<int, (G::KCH == 8 ? 4 : -1)>{});
+            else if (G::KCH == 8 && ns == 6) run(std::integral_constant<int, (G::KCH == 8 ? 6 : -1)>{});
+            else run(std::integral_constant<int, -1>{});
+        } else {
+            run(std::integral_constant<int, -1>{});
+        }
+        // The pairs whose limit falls inside a block's distance range.
+        const uint32_t kbase = lds_addr(kslot(i));
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+            if (const uint64_t part = ~(wprune[kb] | wkeep[kb]))
+                window_partial(sc[kb], part, kbase + (uint32_t)(kb * 32 * G::ROWB), i * kBN + kb * 32);
+        if (need_mask(i)) mask_tile(sc, i);
+    };
     auto scores = [&](int i) __attribute__((always_inline)) {
         if constexpr (WINDOW) {
-            issue(i);
-            qk(sc, i);
-            if (rot_on(i)) rotate_k(i + 1);
+            scores_w(std::true_type{}, i);
         } else {
             if (rot_on(i)) block1(std::true_type{}, i);
             else block1(std::false_type{}, i);
+            if (need_mask(i)) mask_tile(sc, i);
         }
-        if (need_mask(i)) mask_tile(sc, i);
     };
     auto accept = [&](float rs, bf16x8_t (&pn)[kBN / 16]) __attribute__((always_inline)) {
         if (__builtin_amdgcn_ballot_w64(!(rs <= kLazyMaxSum)) != 0) rs = rescale_exp_tile(sc, pn);
@@ -749,20 +871,32 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
     int i = 0;
     if (wave_tiles > 0) {
         // iteration 0: S(0), P(0) into pf_a
-        scores(0);
+        if constexpr (WINDOW) scores_w(std::false_type{}, 0);
+        else scores(0);
         accept(exp_tile(sc, pf_a), pf_a);
         finish(0);
-        // P(j) is in pf_a for even j, in pf_b for odd j.
-        for (i = 1; i + 1 < wave_tiles; i += 2) {
-            steady(i, pf_a, pf_b);
-            steady(i + 1, pf_b, pf_a);
-        }
-        if (i < wave_tiles) {
-            steady(i, pf_a, pf_b);
-            ++i;
-            last_pv(i, pf_b, pf_a);
-        } else {
+        if constexpr (WINDOW) {
+            // One iteration per trip (the window variants make the body
+            // large): P moves from pf_b back to pf_a.
+            for (i = 1; i < wave_tiles; ++i) {
+                steady(i, pf_a, pf_b);
+#pragma unroll
+                for (int ch = 0; ch < kBN / 16; ++ch) pf_a[ch] = pf_b[ch];
+            }
             last_pv(i, pf_a, pf_b);
+        } else {
+            // P(j) is in pf_a for even j, in pf_b for odd j.
+            for (i = 1; i + 1 < wave_tiles; i += 2) {
+                steady(i, pf_a, pf_b);
+                steady(i + 1, pf_b, pf_a);
+            }
+            if (i < wave_tiles) {
+                steady(i, pf_a, pf_b);
+                ++i;
+                last_pv(i, pf_b, pf_a);
+            } else {
+                last_pv(i, pf_a, pf_b);
+            }
         }
         ++i;
     }
