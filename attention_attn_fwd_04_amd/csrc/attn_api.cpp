@@ -72,7 +72,7 @@ int current_device_ok(int *dev_out)
 }
 
 // ---- RoPE cos/sin tables ---------------------------------------------------
-// Built in fp64 on the host and stored as fp32 (layout documented on
+// Built in fp64 on the host and stored rounded to fp16 (layout documented on
 // attn::RopeTable).  One table per (device, D, theta), grown on demand;
 // replaced tables are kept until attn_release because work already enqueued
 // may still read them.
