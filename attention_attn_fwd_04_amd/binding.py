@@ -24,7 +24,7 @@ ATTN_ENOMEM = -4
 ATTN_ELAUNCH = -5
 ATTN_ENODEVICE = -6
 
-EXPORTED = ("attn_fwd", "attn_rope_apply", "attn_window_table", "attn_pruned_terms",
+EXPORTED = ("attn_fwd", "attn_fwd_lse", "attn_rope_apply", "attn_window_table", "attn_pruned_terms",
             "attn_check_args", "attn_strerror", "attn_release")
 
 _lib = None
@@ -49,6 +49,8 @@ def lib():
     i32p = ctypes.POINTER(ctypes.c_int32)
     L.attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, f, i, f, i32p, vp]
     L.attn_fwd.restype = i
+    L.attn_fwd_lse.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, f, i32p, vp]
+    L.attn_fwd_lse.restype = i
     L.attn_rope_apply.argtypes = [vp, vp, vp, vp, i, i, i, i, i, f, vp]
     L.attn_rope_apply.restype = i
     L.attn_window_table.argtypes = [d, i, d, i32p]
@@ -119,6 +121,39 @@ def attn_fwd(q, k, v, o=None, *, rope_theta=10000.0, causal=True, scale=None,
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd")
     return o
+
+
+def attn_fwd_lse(q, k, v, o=None, lse=None, *, rope_theta=10000.0, causal=True, scale=None,
+                 window_table=None, stream=None):
+    """attn_fwd plus the natural-log LSE of every row's scores; returns
+    (o [B,S,Hq,D] bf16, lse [B,Hq,S] fp32)."""
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check_tensor(t, n)
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if k.shape != (B, S, Hkv, D) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, S, Hkv, D] matching q")
+    if o is None:
+        o = torch.empty_like(q)
+    else:
+        _check_tensor(o, "o")
+        if o.shape != q.shape:
+            raise ValueError("o must have q's shape")
+    if lse is None:
+        lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    elif (not isinstance(lse, torch.Tensor) or lse.dtype != torch.float32 or not lse.is_cuda
+          or tuple(lse.shape) != (B, Hq, S) or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 device tensor [B, Hq, S]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    w, wp = _window_ptr(window_table, D)
+    st = lib().attn_fwd_lse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                            B, Hq, Hkv, S, D, float(rope_theta), int(bool(causal)), float(scale), wp,
+                            _stream_handle(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_lse")
+    return o, lse
 
 
 def attn_rope_apply(q, k, q_out=None, k_out=None, *, rope_theta=10000.0, stream=None):

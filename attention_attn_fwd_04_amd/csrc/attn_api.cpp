@@ -161,6 +161,38 @@ int check_window(const int32_t *w, int D, int causal)
     return ATTN_OK;
 }
 
+int fwd_common(const void *q, const void *k, const void *v, void *o, float *lse, int B, int Hq, int Hkv, int S,
+               int D, float rope_theta, int causal, float scale, const int32_t *window_table, void *stream)
+{
+    int st = attn_check_args(q, k, v, o, B, Hq, Hkv, S, D, rope_theta, causal, scale, window_table);
+    if (st != ATTN_OK) return st;
+    int dev = -1;
+    st = current_device_ok(&dev);
+    if (st != ATTN_OK) return st;
+    if (B == 0 || S == 0) return ATTN_OK;
+
+    attn::FwdArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.q = static_cast<const uint16_t *>(q);
+    a.k = static_cast<const uint16_t *>(k);
+    a.v = static_cast<const uint16_t *>(v);
+    a.o = static_cast<uint16_t *>(o);
+    a.lse = lse;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.S = S; a.D = D;
+    a.causal = causal;
+    a.scale_log2e = (float)((double)scale * 1.4426950408889634073599246810019);
+    if (window_table) {
+        a.use_window = 1;
+        for (int r = 0; r < D / 2; ++r) a.window[r] = window_table[r];
+    }
+    if (rope_theta != 0.0f) {
+        st = get_table(dev, D, rope_theta, S, &a.rope_cs);
+        if (st != ATTN_OK) return st;
+    }
+    if (attn::launch_attn_fwd(a, static_cast<hipStream_t>(stream)) != hipSuccess) return ATTN_ELAUNCH;
+    return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -171,7 +203,7 @@ const char *attn_strerror(int status)
     case ATTN_OK: return "success";
     case ATTN_EINVAL: return "invalid argument";
     case ATTN_EUNSUPPORTED: return "unsupported configuration (head dimension must be 64 or 128)";
-    case ATTN_EALIGN: return "tensor pointer not 16-byte aligned";
+    case ATTN_EALIGN: return "pointer not aligned (tensors: 16 bytes, lse: 4 bytes)";
     case ATTN_ENOMEM: return "device allocation failed";
     case ATTN_ELAUNCH: return "HIP runtime error while launching or copying";
     case ATTN_ENODEVICE: return "no gfx950 HIP device is current";
@@ -197,35 +229,29 @@ int attn_check_args(const void *q, const void *k, const void *v, const void *o, 
     return check_window(window_table, D, causal);
 }
 
+
 int attn_fwd(const void *q, const void *k, const void *v, void *o, int B, int Hq, int Hkv, int S, int D,
              float rope_theta, int causal, float scale, const int32_t *window_table, void *stream)
 {
-    int st = attn_check_args(q, k, v, o, B, Hq, Hkv, S, D, rope_theta, causal, scale, window_table);
-    if (st != ATTN_OK) return st;
-    int dev = -1;
-    st = current_device_ok(&dev);
-    if (st != ATTN_OK) return st;
-    if (B == 0 || S == 0) return ATTN_OK;
+    return fwd_common(q, k, v, o, nullptr, B, Hq, Hkv, S, D, rope_theta, causal, scale, window_table, stream);
+}
 
-    attn::FwdArgs a;
-    std::memset(&a, 0, sizeof a);
-    a.q = static_cast<const uint16_t *>(q);
-    a.k = static_cast<const uint16_t *>(k);
-    a.v = static_cast<const uint16_t *>(v);
-    a.o = static_cast<uint16_t *>(o);
-    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.S = S; a.D = D;
-    a.causal = causal;
-    a.scale_log2e = (float)((double)scale * 1.4426950408889634073599246810019);
-    if (window_table) {
-        a.use_window = 1;
-        for (int r = 0; r < D / 2; ++r) a.window[r] = window_table[r];
+int attn_fwd_lse(const void *q, const void *k, const void *v, void *o, float *lse, int B, int Hq, int Hkv, int S,
+                 int D, float rope_theta, int causal, float scale, const int32_t *window_table, void *stream)
+{
+    const bool empty = (B <= 0 || S <= 0);
+    if (!empty) {
+        if (lse == nullptr) return ATTN_EINVAL;
+        if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return ATTN_EALIGN;
+        if (B > 0 && Hq > 0 && S > 0 && D > 0) {
+            const size_t nl = (size_t)B * Hq * S * 4, nq = (size_t)B * S * Hq * D * 2;
+            const size_t nkv = (Hkv > 0) ? (size_t)B * S * Hkv * D * 2 : 0;
+            if (overlaps(lse, nl, q, nq) || overlaps(lse, nl, k, nkv) || overlaps(lse, nl, v, nkv) ||
+                overlaps(lse, nl, o, nq))
+                return ATTN_EINVAL;
+        }
     }
-    if (rope_theta != 0.0f) {
-        st = get_table(dev, D, rope_theta, S, &a.rope_cs);
-        if (st != ATTN_OK) return st;
-    }
-    if (attn::launch_attn_fwd(a, static_cast<hipStream_t>(stream)) != hipSuccess) return ATTN_ELAUNCH;
-    return ATTN_OK;
+    return fwd_common(q, k, v, o, lse, B, Hq, Hkv, S, D, rope_theta, causal, scale, window_table, stream);
 }
 
 int attn_rope_apply(const void *q, const void *k, void *q_out, void *k_out, int B, int Hq, int Hkv, int S,

@@ -905,9 +905,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
 
     // ---- epilogue: O / l, bf16, store --------------------------------------
     if (!wave_active) return;
-    const float inv = 1.0f / sum_halves(l_run);
+    const float l_row = sum_halves(l_run);
+    const float inv = 1.0f / l_row;
     const int n = nw0 + l32;
     if (n >= S) return;
+    // Optional log-sum-exp of the row's scaled scores, L = m + log l in the
+    // natural-log domain ("AttnFuse", section 4.4: the one value per row the
+    // forward pass keeps for a backward pass): sum_m 2^(s c) = 2^(m_ref c) l.
+    if (a.lse != nullptr && g == 0)
+        a.lse[((size_t)b * a.Hq + hq) * S + n] =
+            (m_ref * c + __builtin_amdgcn_logf(l_row)) * 0.693147180559945309f;
     uint16_t *orow = og + (size_t)n * a.Hq * D;
 #pragma unroll
     for (int db = 0; db < G::DB; ++db)

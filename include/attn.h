@@ -44,7 +44,7 @@ typedef enum {
     ATTN_OK = 0,
     ATTN_EINVAL = -1,       /* bad argument (NULL, negative size, Hq % Hkv, scale, ...) */
     ATTN_EUNSUPPORTED = -2, /* valid but not built: D not in {64, 128} */
-    ATTN_EALIGN = -3,       /* a tensor pointer is not 16-byte aligned */
+    ATTN_EALIGN = -3,       /* a tensor pointer is not 16-byte aligned (lse: 4-byte) */
     ATTN_ENOMEM = -4,       /* device allocation of the cos/sin table failed */
     ATTN_ELAUNCH = -5,      /* the HIP runtime refused the launch or a copy */
     ATTN_ENODEVICE = -6     /* no HIP device / the current device is not gfx950 */
@@ -75,6 +75,29 @@ int attn_fwd(const void *q, const void *k, const void *v, void *o,
              int B, int Hq, int Hkv, int S, int D,
              float rope_theta, int causal, float scale,
              const int32_t *window_table, void *stream);
+
+/*
+ * attn_fwd that also writes, for every query row, the natural-log
+ * log-sum-exp of its (masked, windowed) scaled scores,
+ *
+ *   lse[b, hq, n] = log sum_m exp(scale * <R(n) q, R(m) k>),
+ *
+ * i.e. L = m + log l of the online softmax: the one value per row that a
+ * forward pass keeps so that a backward pass can rebuild the softmax
+ * probabilities tile by tile, and that partial results over disjoint key
+ * ranges need to be merged ("AttnFuse", section 4.4 "Backward Pass" and
+ * section 4.2 "Flash Decoding").
+ *
+ *  lse: fp32 device pointer to [B, Hq, S] (row-major, caller-owned, 4-byte
+ *       aligned, not overlapping q, k, v or o); NULL is rejected unless B or
+ *       S is 0.  All other arguments and errors are those of attn_fwd, and o
+ *       is bitwise the same as attn_fwd's.  l is the sum of the
+ *       bf16-rounded probabilities that also enter P V.
+ */
+int attn_fwd_lse(const void *q, const void *k, const void *v, void *o, float *lse,
+                 int B, int Hq, int Hkv, int S, int D,
+                 float rope_theta, int causal, float scale,
+                 const int32_t *window_table, void *stream);
 
 /*
  * The separate RoPE pass ("AttnFuse", section 1 and Figure 1(a): rotate Q

@@ -121,3 +121,20 @@ def test_window_table_argument_errors():
     for args in ((1.0, 128, 2.0), (5e5, 127, 2.0), (5e5, 128, 0.0), (float("nan"), 128, 2.0)):
         with pytest.raises(binding.AttnError):
             binding.attn_window_table(*args)
+
+
+def _lse_call(lse, S=128):
+    """attn_fwd_lse with fake device addresses: only argument errors that are
+    caught before any device call are exercised here."""
+    return binding.lib().attn_fwd_lse(A, A * 64, A * 128, A * 192, lse, 1, 4, 2, S, 128,
+                                      1e4, 1, 0.088, None, None)
+
+
+@pytest.mark.parametrize("lse,status", [
+    (0, binding.ATTN_EINVAL),              # no lse buffer
+    (A * 256 + 2, binding.ATTN_EALIGN),    # lse not 4-byte aligned
+    (A * 192 + 64, binding.ATTN_EINVAL),   # lse overlaps o
+    (A + 4096, binding.ATTN_EINVAL),       # lse overlaps q
+])
+def test_fwd_lse_rejects_bad_lse(lse, status):
+    assert _lse_call(lse) == status

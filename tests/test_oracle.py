@@ -321,3 +321,72 @@ def test_printed_softmax_constant_and_flop_formula():
     for row in g["fa3_rows"]:
         flops = 2 * w["B"] * w["H"] * row["S"] ** 2 * w["D"]
         assert abs(flops / (row["ms"] * 1e9) - row["tflops"]) < 0.05
+
+
+# --------------------------------------------------------------------------
+# Log-sum-exp of each row's scaled scores (the L = m + log l a forward pass
+# keeps for the backward pass and for merging partial results: "AttnFuse",
+# sections 4.2 and 4.4).
+# --------------------------------------------------------------------------
+def _all_lse(q, k, v, theta, causal, scale, window=None):
+    B, S, Hq, _ = q.shape
+    rows = O.all_rows(B, S, Hq)
+    _, lse = O.attn_rows(q, k, v, rows, theta, causal, scale, window, want_lse=True)
+    return lse.reshape(B, S, Hq)
+
+
+@pytest.mark.parametrize("B,S,Hq,Hkv,D,theta,causal", [
+    (1, 40, 2, 2, 64, 1e4, True),
+    (2, 29, 4, 2, 64, 5e5, True),
+    (1, 33, 2, 1, 128, 1e4, False),
+    (1, 24, 2, 2, 64, 0.0, True),
+])
+def test_lse_matches_torch_logsumexp_fp64(B, S, Hq, Hkv, D, theta, causal):
+    """Library special case: scores from transformers-rotated inputs by a
+    torch fp64 matmul, masked, reduced by torch.logsumexp."""
+    from transformers.models.llama.modeling_llama import apply_rotary_pos_emb
+    q, k, v = _qkv_np(B, S, Hq, Hkv, D, seed=300 + S)
+    scale = 1 / math.sqrt(D)
+    qt = torch.from_numpy(_f64(q)).permute(0, 2, 1, 3)
+    kt = torch.from_numpy(_f64(k)).permute(0, 2, 1, 3)
+    if theta:
+        inv = 1.0 / (theta ** (torch.arange(0, D, 2, dtype=torch.float64) / D))
+        fr = torch.arange(S, dtype=torch.float64)[:, None] * inv[None, :]
+        emb = torch.cat([fr, fr], -1)
+        qt, kt = apply_rotary_pos_emb(qt, kt, emb.cos()[None], emb.sin()[None], unsqueeze_dim=1)
+    kt = kt.repeat_interleave(Hq // Hkv, dim=1)
+    sc = scale * torch.matmul(qt, kt.transpose(-1, -2).contiguous())
+    if causal:
+        sc = sc.masked_fill(~torch.ones(S, S, dtype=torch.bool).tril(), float("-inf"))
+    ref = torch.logsumexp(sc, dim=-1).permute(0, 2, 1).numpy()   # [B, S, Hq]
+    np.testing.assert_allclose(_all_lse(q, k, v, theta, causal, scale), ref, rtol=0, atol=1e-12)
+
+
+def test_lse_closed_forms():
+    """Q = 0: every score is 0, so L = log(number of keys) = log(n + 1) under
+    the causal mask and log S without it.  Causal row 0 sees only key 0, and
+    position 0 is not rotated: L = scale * q0 . k0 exactly."""
+    B, S, H, D = 1, 30, 2, 64
+    q, k, v = _qkv_np(B, S, H, H, D, seed=31)
+    zq = np.zeros_like(q)
+    lc = _all_lse(zq, k, v, 1e4, True, 0.125)
+    np.testing.assert_allclose(lc, np.broadcast_to(np.log(np.arange(1, S + 1))[None, :, None], lc.shape),
+                               rtol=0, atol=1e-14)
+    ln = _all_lse(zq, k, v, 1e4, False, 0.125)
+    np.testing.assert_allclose(ln, np.full(ln.shape, math.log(S)), rtol=0, atol=1e-14)
+    l0 = _all_lse(q, k, v, 1e4, True, 0.125)[:, 0, :]
+    for h in range(H):
+        exact = 0.125 * float(np.dot(_f64(q)[0, 0, h], _f64(k)[0, 0, h]))
+        assert abs(l0[0, h] - exact) <= 1e-15 * max(1.0, abs(exact))
+
+
+def test_lse_window_matches_brute_force_scores():
+    """Window on: L from the independent per-pair brute-force scores."""
+    S, D = 20, 16
+    q, k, v = _qkv_np(1, S, 1, 1, D, seed=32)
+    window = np.array([0, 1, 3, 4, 7, 9, 15, 30], dtype=np.int32)
+    _, sc = brute.attention_head(_f64(q)[0, :, 0], _f64(k)[0, :, 0], _f64(v)[0, :, 0],
+                                 1e4, True, 0.25, window)
+    mx = sc.max(axis=1, keepdims=True)
+    ref = (mx + np.log(np.exp(sc - mx).sum(axis=1, keepdims=True)))[:, 0]
+    np.testing.assert_allclose(_all_lse(q, k, v, 1e4, True, 0.25, window)[0, :, 0], ref, rtol=0, atol=1e-13)
