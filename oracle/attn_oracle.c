@@ -211,6 +211,64 @@ int oracle_attn_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
 }
 
 /*
+ * Decode ("AttnFuse", section 4.2 "Flash Decoding"): one new query per
+ * sequence, at position L-1 (+ pos_offset), against a cache of L keys and
+ * values.  The cache holds keys as they were stored (rotated when they were
+ * appended); only the query is rotated here.  Every key 0..L-1 is visible;
+ * with a window, pair r counts for key m only when (L-1) - m <= w[r].
+ *   q: [B, Hq, D]; k, v: [B, L, Hkv, D]; out: [B, Hq, D] fp64;
+ *   lse: optional [B, Hq] natural-log log-sum-exp of the scaled scores.
+ */
+int oracle_decode(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                  int B, int L, int Hq, int Hkv, int D, double rope_theta,
+                  double scale, const int32_t *window, long long pos_offset,
+                  double *out, double *lse)
+{
+    if (B < 0 || L <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || D > 1024 ||
+        (D % 2) != 0 || (Hq % Hkv) != 0)
+        return -1;
+    int group = Hq / Hkv;
+    long long n = (long long)L - 1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long long bh = 0; bh < (long long)B * Hq; ++bh) {
+        int b = (int)(bh / Hq), hq = (int)(bh % Hq), hk = hq / group;
+        double qraw[1024], qr[1024], kr[1024];
+        const uint16_t *qs = q + ((size_t)b * Hq + hq) * (size_t)D;
+        for (int d = 0; d < D; ++d)
+            qraw[d] = widen_bf16(qs[d]);
+        rotate_row(qraw, D, rope_theta, (double)(n + pos_offset), qr);
+        double *srow = (double *)malloc(sizeof(double) * (size_t)L);
+        double mu = -INFINITY;
+        for (int m = 0; m < L; ++m) {
+            const uint16_t *ks = row_ptr(k, L, Hkv, D, b, m, hk);
+            for (int d = 0; d < D; ++d)
+                kr[d] = widen_bf16(ks[d]);
+            srow[m] = score(qr, kr, D, scale, window, n - (long long)m);
+            if (srow[m] > mu)
+                mu = srow[m];
+        }
+        double z = 0.0;
+        for (int m = 0; m < L; ++m) {
+            srow[m] = exp(srow[m] - mu);
+            z += srow[m];
+        }
+        double *o = out + (size_t)bh * D;
+        for (int d = 0; d < D; ++d)
+            o[d] = 0.0;
+        for (int m = 0; m < L; ++m) {
+            double p = srow[m] / z;
+            const uint16_t *vs = row_ptr(v, L, Hkv, D, b, m, hk);
+            for (int d = 0; d < D; ++d)
+                o[d] += p * widen_bf16(vs[d]);
+        }
+        if (lse)
+            lse[bh] = mu + log(z);
+        free(srow);
+    }
+    return 0;
+}
+
+/*
  * The scaled score row s(n, m) for m = 0..S-1 of one query (b, n, hq), with
  * masked keys (m > n under the causal mask) set to -inf.  Used by the
  * invariance and window tests.

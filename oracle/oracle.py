@@ -49,6 +49,10 @@ def _load():
                                      i32p, ctypes.c_longlong, i32p, ctypes.c_longlong,
                                      f64p, f64p]
     lib.oracle_attn_rows.restype = ctypes.c_int
+    lib.oracle_decode.argtypes = [u16p, u16p, u16p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_double,
+                                  i32p, ctypes.c_longlong, f64p, f64p]
+    lib.oracle_decode.restype = ctypes.c_int
     lib.oracle_scores_row.argtypes = [u16p, u16p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                       ctypes.c_int, ctypes.c_int, ctypes.c_double,
                                       ctypes.c_int, ctypes.c_double, i32p,
@@ -106,6 +110,26 @@ def attn_rows(q, k, v, rows, rope_theta, causal, scale, window=None, pos_offset=
                               lse.ctypes.data_as(ctypes.POINTER(ctypes.c_double)) if want_lse else None)
     if rc != 0:
         raise ValueError("oracle_attn_rows rejected its arguments")
+    return (out, lse) if want_lse else out
+
+
+def decode(q, k, v, rope_theta, scale, window=None, pos_offset=0, want_lse=False):
+    """Decode attention (fp64): q uint16 [B, Hq, D] at position L-1 against the
+    cache k, v uint16 [B, L, Hkv, D] (keys used as stored).  Returns
+    [B, Hq, D] (and the natural-log LSE [B, Hq] when want_lse)."""
+    lib = _load()
+    B, Hq, D = q.shape
+    L, Hkv = k.shape[1], k.shape[2]
+    assert k.shape == (B, L, Hkv, D) and v.shape == k.shape
+    q, k, v = (np.ascontiguousarray(t) for t in (q, k, v))
+    out = np.zeros((B, Hq, D), dtype=np.float64)
+    lse = np.zeros((B, Hq), dtype=np.float64) if want_lse else None
+    w, wp = _window_arg(window, D)
+    rc = lib.oracle_decode(_u16(q), _u16(k), _u16(v), B, L, Hq, Hkv, D, float(rope_theta), float(scale),
+                           wp, int(pos_offset), out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+                           lse.ctypes.data_as(ctypes.POINTER(ctypes.c_double)) if want_lse else None)
+    if rc != 0:
+        raise ValueError("oracle_decode rejected its arguments")
     return (out, lse) if want_lse else out
 
 

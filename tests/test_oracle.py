@@ -390,3 +390,71 @@ def test_lse_window_matches_brute_force_scores():
     mx = sc.max(axis=1, keepdims=True)
     ref = (mx + np.log(np.exp(sc - mx).sum(axis=1, keepdims=True)))[:, 0]
     np.testing.assert_allclose(_all_lse(q, k, v, 1e4, True, 0.25, window)[0, :, 0], ref, rtol=0, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# Decode ("AttnFuse", section 4.2): one query at position L-1 against a cache
+# whose keys are used as stored.
+# --------------------------------------------------------------------------
+def _decode_inputs(B, L, Hq, Hkv, D, seed):
+    q, k, v = make_qkv(B, L, Hq, Hkv, D, seed)
+    qb = bf16_bits(q)[:, -1].copy()          # [B, Hq, D]: the newest token's queries
+    return qb, bf16_bits(k), bf16_bits(v)
+
+
+@pytest.mark.parametrize("B,L,Hq,Hkv,D,theta", [
+    (1, 37, 8, 2, 64, 1e4),
+    (2, 50, 4, 4, 128, 5e5),
+    (1, 29, 6, 1, 64, 0.0),
+])
+def test_decode_matches_torch_sdpa_fp64(B, L, Hq, Hkv, D, theta):
+    """Library special case: the query rotated by the transformers routine at
+    position L-1, the cache keys as given, torch fp64 SDPA over all L keys."""
+    from transformers.models.llama.modeling_llama import apply_rotary_pos_emb
+    q, k, v = _decode_inputs(B, L, Hq, Hkv, D, seed=400 + L)
+    scale = 1 / math.sqrt(D)
+    qt = torch.from_numpy(_f64(q))[:, :, None, :]               # B H 1 D
+    if theta:
+        inv = 1.0 / (theta ** (torch.arange(0, D, 2, dtype=torch.float64) / D))
+        fr = torch.tensor([float(L - 1)], dtype=torch.float64)[:, None] * inv[None, :]
+        emb = torch.cat([fr, fr], -1)
+        qt, _ = apply_rotary_pos_emb(qt, qt, emb.cos()[None], emb.sin()[None], unsqueeze_dim=1)
+    kt = torch.from_numpy(_f64(k)).permute(0, 2, 1, 3).contiguous()
+    vt = torch.from_numpy(_f64(v)).permute(0, 2, 1, 3).contiguous()
+    ref = torch.nn.functional.scaled_dot_product_attention(qt.contiguous(), kt, vt, scale=scale,
+                                                           enable_gqa=(Hq != Hkv))[:, :, 0].numpy()
+    out, lse = O.decode(q, k, v, theta, scale, want_lse=True)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+    kg = kt.repeat_interleave(Hq // Hkv, dim=1)
+    ref_lse = torch.logsumexp(scale * torch.matmul(qt, kg.transpose(-1, -2).contiguous())[:, :, 0], dim=-1).numpy()
+    np.testing.assert_allclose(lse, ref_lse, rtol=0, atol=1e-12)
+
+
+def test_decode_closed_forms():
+    """L = 1 returns V[0] exactly; Q = 0 and an all-pruned window (w = -1)
+    give the mean of V over the cache."""
+    B, L, H, D = 1, 23, 2, 64
+    q, k, v = _decode_inputs(B, L, H, H, D, seed=41)
+    vf = _f64(v)
+    one = O.decode(q, k[:, :1].copy(), v[:, :1].copy(), 1e4, 0.125)
+    np.testing.assert_array_equal(one, vf[:, 0])
+    mean = np.broadcast_to(vf.mean(axis=1), (B, H, D))
+    np.testing.assert_allclose(O.decode(np.zeros_like(q), k, v, 1e4, 0.125), mean, rtol=0, atol=1e-14)
+    w = np.full(D // 2, -1, dtype=np.int32)
+    np.testing.assert_allclose(O.decode(q, k, v, 1e4, 0.125, w), mean, rtol=0, atol=1e-14)
+
+
+def test_decode_window_matches_brute_force():
+    """Per-pair window on the decode row, from the brute force's explicit
+    rotation and per-pair terms."""
+    L, D = 40, 16
+    q, k, v = _decode_inputs(1, L, 1, 1, D, seed=42)
+    window = np.array([0, 2, 3, 5, 8, 13, 21, 34], dtype=np.int32)
+    qr = brute.rotate(_f64(q)[0], 1e4, np.array([L - 1]))          # [1, D]
+    terms = brute.pair_terms(qr, _f64(k)[0, :, 0])[0]               # [L, D/2]
+    dist = (L - 1) - np.arange(L)
+    terms = np.where(dist[:, None] <= window[None, :], terms, 0.0)
+    s = 0.3 * terms.sum(axis=1)
+    p = np.exp(s - s.max())
+    ref = (p / p.sum()) @ _f64(v)[0, :, 0]
+    np.testing.assert_allclose(O.decode(q, k, v, 1e4, 0.3, window)[0, 0], ref, rtol=0, atol=1e-13)
