@@ -24,7 +24,7 @@ ATTN_ENOMEM = -4
 ATTN_ELAUNCH = -5
 ATTN_ENODEVICE = -6
 
-EXPORTED = ("attn_fwd", "attn_fwd_lse", "attn_rope_apply", "attn_window_table", "attn_pruned_terms",
+EXPORTED = ("attn_fwd", "attn_fwd_lse", "attn_decode", "attn_decode_workspace_bytes", "attn_rope_apply", "attn_window_table", "attn_pruned_terms",
             "attn_check_args", "attn_strerror", "attn_release")
 
 _lib = None
@@ -51,6 +51,10 @@ def lib():
     L.attn_fwd.restype = i
     L.attn_fwd_lse.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, f, i32p, vp]
     L.attn_fwd_lse.restype = i
+    L.attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i, i, i, i, i, f, f, i32p, i, vp]
+    L.attn_decode.restype = i
+    L.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    L.attn_decode_workspace_bytes.restype = ctypes.c_size_t
     L.attn_rope_apply.argtypes = [vp, vp, vp, vp, i, i, i, i, i, f, vp]
     L.attn_rope_apply.restype = i
     L.attn_window_table.argtypes = [d, i, d, i32p]
@@ -154,6 +158,49 @@ def attn_fwd_lse(q, k, v, o=None, lse=None, *, rope_theta=10000.0, causal=True, 
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd_lse")
     return o, lse
+
+
+def attn_decode_workspace_bytes(B, Hq, Hkv, L, D, num_splits=0) -> int:
+    return int(lib().attn_decode_workspace_bytes(int(B), int(Hq), int(Hkv), int(L), int(D), int(num_splits)))
+
+
+def attn_decode(q, k, v, o=None, lse=None, workspace=None, *, rope_theta=10000.0, scale=None,
+                window_table=None, num_splits=0, want_lse=False, stream=None):
+    """Split-KV decode: q [B, Hq, D] (the token at position L-1) against the
+    cache k, v [B, L, Hkv, D]; returns o [B, Hq, D] (and lse [B, Hq] fp32 when
+    want_lse or an lse buffer is given)."""
+    import torch
+    for t, n in ((k, "k"), (v, "v")):
+        _check_tensor(t, n)
+    B, L, Hkv, D = k.shape
+    if v.shape != k.shape:
+        raise ValueError("v must match k [B, L, Hkv, D]")
+    if (not isinstance(q, torch.Tensor) or q.dtype != torch.bfloat16 or q.dim() != 3 or not q.is_cuda
+            or not q.is_contiguous() or q.shape[0] != B or q.shape[2] != D):
+        raise ValueError("q must be a contiguous bfloat16 device tensor [B, Hq, D]")
+    Hq = q.shape[1]
+    if o is None:
+        o = torch.empty_like(q)
+    elif o.shape != q.shape or o.dtype != torch.bfloat16 or not o.is_contiguous():
+        raise ValueError("o must be a contiguous bfloat16 tensor shaped like q")
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq) or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 tensor [B, Hq]")
+    nbytes = attn_decode_workspace_bytes(B, Hq, Hkv, L, D, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    w, wp = _window_ptr(window_table, D)
+    st = lib().attn_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                           lse.data_ptr() if lse is not None else None,
+                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                           B, Hq, Hkv, L, D, float(rope_theta), float(scale), wp, int(num_splits),
+                           _stream_handle(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_decode")
+    return (o, lse) if lse is not None else o
 
 
 def attn_rope_apply(q, k, q_out=None, k_out=None, *, rope_theta=10000.0, stream=None):

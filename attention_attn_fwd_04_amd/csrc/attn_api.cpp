@@ -193,6 +193,31 @@ int fwd_common(const void *q, const void *k, const void *v, void *o, float *lse,
     return ATTN_OK;
 }
 
+// Split count of attn_decode: num_splits > 0 as asked (at most one split per
+// 32 keys and at most kMaxDecodeSplits), otherwise enough splits for about
+// 1024 waves over the whole batch (one resident round at four waves per CU),
+// each split at least 64 keys.  Keys per split are a multiple of 32,
+// and every split is non-empty.
+void decode_plan(int B, int Hkv, int L, int num_splits, int *n_split, int *keys_per_split)
+{
+    const int max_split = (L + 31) / 32;
+    int n = num_splits;
+    if (n <= 0) {
+        const long long groups = (long long)B * Hkv;
+        long long want = (1024 + groups - 1) / (groups > 0 ? groups : 1);
+        const int cap = (L + 63) / 64;
+        if (want > cap) want = cap;
+        n = (int)(want < 1 ? 1 : want);
+    }
+    if (n > max_split) n = max_split;
+    if (n > attn::kMaxDecodeSplits) n = attn::kMaxDecodeSplits;
+    if (n < 1) n = 1;
+    int kps = (L + n - 1) / n;
+    kps = (kps + 31) / 32 * 32;
+    *keys_per_split = kps;
+    *n_split = (L + kps - 1) / kps;
+}
+
 }  // namespace
 
 extern "C" {
@@ -252,6 +277,76 @@ int attn_fwd_lse(const void *q, const void *k, const void *v, void *o, float *ls
         }
     }
     return fwd_common(q, k, v, o, lse, B, Hq, Hkv, S, D, rope_theta, causal, scale, window_table, stream);
+}
+
+size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int L, int D, int num_splits)
+{
+    if (B <= 0 || L <= 0 || Hq < 1 || Hkv < 1 || D <= 0 || num_splits < 0) return 0;
+    int n_split = 1, kps = 32;
+    decode_plan(B, Hkv, L, num_splits, &n_split, &kps);
+    // partial outputs, then the (m, l) pairs; 256-byte aligned sections
+    const size_t po = ((size_t)B * Hq * n_split * D * 4 + 255) / 256 * 256;
+    const size_t ml = (size_t)B * Hq * n_split * 2 * 4;
+    return po + ml;
+}
+
+int attn_decode(const void *q, const void *k, const void *v, void *o, float *lse, void *workspace,
+                size_t workspace_bytes, int B, int Hq, int Hkv, int L, int D, float rope_theta, float scale,
+                const int32_t *window_table, int num_splits, void *stream)
+{
+    int st = check_shapes(B, Hq, Hkv, L, D);
+    if (st != ATTN_OK) return st;
+    if (Hq / Hkv > 32) return ATTN_EUNSUPPORTED;   // query heads per KV head: one MFMA's 32 columns
+    if (num_splits < 0) return ATTN_EINVAL;
+    const bool empty = (B == 0 || L == 0);
+    if (!empty && (!q || !k || !v || !o || !workspace)) return ATTN_EINVAL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(workspace))
+        return ATTN_EALIGN;
+    if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return ATTN_EALIGN;
+    if (!std::isfinite(scale) || !(scale > 0.0f)) return ATTN_EINVAL;
+    st = check_theta(rope_theta);
+    if (st != ATTN_OK) return st;
+    st = check_window(window_table, D, 1);
+    if (st != ATTN_OK) return st;
+    if (empty) return ATTN_OK;
+    if (workspace_bytes < attn_decode_workspace_bytes(B, Hq, Hkv, L, D, num_splits)) return ATTN_EINVAL;
+    const size_t nq = (size_t)B * Hq * D * 2, nkv = (size_t)B * L * Hkv * D * 2;
+    const size_t nws = attn_decode_workspace_bytes(B, Hq, Hkv, L, D, num_splits);
+    const size_t nl = (size_t)B * Hq * 4;
+    if (overlaps(o, nq, q, nq) || overlaps(o, nq, k, nkv) || overlaps(o, nq, v, nkv) ||
+        overlaps(workspace, nws, q, nq) || overlaps(workspace, nws, k, nkv) || overlaps(workspace, nws, v, nkv) ||
+        overlaps(workspace, nws, o, nq))
+        return ATTN_EINVAL;
+    if (lse && (overlaps(lse, nl, q, nq) || overlaps(lse, nl, k, nkv) || overlaps(lse, nl, v, nkv) ||
+                overlaps(lse, nl, o, nq) || overlaps(lse, nl, workspace, nws)))
+        return ATTN_EINVAL;
+    int dev = -1;
+    st = current_device_ok(&dev);
+    if (st != ATTN_OK) return st;
+
+    attn::DecodeArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.q = static_cast<const uint16_t *>(q);
+    a.k = static_cast<const uint16_t *>(k);
+    a.v = static_cast<const uint16_t *>(v);
+    a.o = static_cast<uint16_t *>(o);
+    a.lse = lse;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.L = L; a.D = D;
+    decode_plan(B, Hkv, L, num_splits, &a.n_split, &a.keys_per_split);
+    const size_t po = ((size_t)B * Hq * a.n_split * D * 4 + 255) / 256 * 256;
+    a.part_o = static_cast<float *>(workspace);
+    a.part_ml = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + po);
+    a.scale_log2e = (float)((double)scale * 1.4426950408889634073599246810019);
+    if (window_table) {
+        a.use_window = 1;
+        for (int r = 0; r < D / 2; ++r) a.window[r] = window_table[r];
+    }
+    if (rope_theta != 0.0f) {
+        st = get_table(dev, D, rope_theta, L, &a.rope_cs);
+        if (st != ATTN_OK) return st;
+    }
+    if (attn::launch_decode(a, static_cast<hipStream_t>(stream)) != hipSuccess) return ATTN_ELAUNCH;
+    return ATTN_OK;
 }
 
 int attn_rope_apply(const void *q, const void *k, void *q_out, void *k_out, int B, int Hq, int Hkv, int S,

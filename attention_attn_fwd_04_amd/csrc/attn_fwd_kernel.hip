@@ -57,21 +57,11 @@
 
 #include <type_traits>
 
+#include "attn_gfx950.h"
 #include "attn_internal.h"
 
 namespace attn {
 namespace {
-
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
-typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
-typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4_t;
-typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
-typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8_t;
-typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
-
-// 32-bit LDS address <-> LDS pointer.
-__device__ __forceinline__ uint32_t lds_addr(const void *p) { return (uint32_t)(uintptr_t)(const lds_u8_t *)p; }
-__device__ __forceinline__ const lds_u8_t *lds_ptr(uint32_t a) { return (const lds_u8_t *)(uintptr_t)a; }
 
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
@@ -114,143 +104,6 @@ struct Geo {
     static __device__ __forceinline__ int vx(int r) { return D == 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2); }
     static __device__ __forceinline__ int v_off(int r, int c) { return r * ROWB + ((c ^ vx(r)) << 4); }
 };
-
-// v_permlane32_swap exchanges lanes 0..31 of one register with lanes 32..63
-// of another.  Swapping x with itself leaves {x[l], x[l ^ 32]} in the two
-// results of every lane l, so their max / sum is the reduction over the two
-// lane halves, identical in both halves.
-__device__ __forceinline__ float max_halves(float x)
-{
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float sum_halves(float x)
-{
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// acc + lo + hi of a packed pair of bf16 values (v_dot2_f32_bf16 against
-// (1, 1)).  The row sums l add up the bf16-rounded P that the PV MFMAs use.
-__device__ __forceinline__ float sum_bf16x2(uint32_t pair, float acc)
-{
-    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pair), bf16x2_t{(__bf16)1.0f, (__bf16)1.0f},
-                                           acc, false);
-}
-
-// Buffer resource over [base, base + bytes); loads beyond it return zero.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off)
-{
-    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
-}
-__device__ __forceinline__ float4 bload16f(__amdgpu_buffer_rsrc_t r, uint32_t off)
-{
-    return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
-}
-
-template <typename T>
-__device__ __forceinline__ T &lds_at(uint8_t *base, int off) { return *reinterpret_cast<T *>(base + off); }
-
-// Buffer load of 16 bytes per lane straight into LDS: lane i writes
-// lds_base + 16 i (lds_base wave-uniform, passed in M0).  Out-of-range lanes
-// write zeros.  Issued through inline assembly so that the compiler does not
-// treat these asynchronous LDS writes as pending on every later LDS read and
-// barrier; the kernel waits for them itself (wait_vmcnt) before the barrier
-// that publishes the tile.  One wait state separates the M0 write from its use.
-// The same kind of buffer resource as four 32-bit words (base, stride 0,
-// size, flags), for the inline assembly below, which takes it as a scalar
-// operand.
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ u32x4_t make_desc(const void *base, uint32_t bytes)
-{
-    const uint64_t p = (uint64_t)(uintptr_t)base;
-    u32x4_t d;
-    d.x = (uint32_t)p;
-    d.y = (uint32_t)(p >> 32) & 0xffffu;
-    d.z = bytes;
-    d.w = 0x00020000u;
-    return d;
-}
-
-__device__ __forceinline__ void dma16(u32x4_t r, uint32_t voff, const uint8_t *lds_base)
-{
-    // Both scalar operands pass through readfirstlane: free when the value
-    // already lives in SGPRs, one v_readfirstlane per word when register
-    // allocation moved it to a VGPR (the asm operands must be SGPRs).
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)lds_base);
-    u32x4_t rs;
-    rs.x = __builtin_amdgcn_readfirstlane(r.x);
-    rs.y = __builtin_amdgcn_readfirstlane(r.y);
-    rs.z = __builtin_amdgcn_readfirstlane(r.z);
-    rs.w = __builtin_amdgcn_readfirstlane(r.w);
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-                 :
-                 : "v"(voff), "s"(rs), "s"(m0)
-                 : "memory", "m0");
-}
-
-// s_waitcnt on the vector-memory counter only: at most n loads of this wave
-// still in flight (loads retire in issue order).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-// Zero the pairs of an 8-pair K operand chunk whose bit in keep_bits is clear
-// (element e of the chunk belongs to pair e of the 8 in both lane halves).
-__device__ __forceinline__ bf16x8_t mask_pairs(bf16x8_t x, uint32_t keep_bits)
-{
-    uint4 u = __builtin_bit_cast(uint4, x);
-    uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t m = ((keep_bits >> (2 * i)) & 1u ? 0x0000ffffu : 0u) |
-                           ((keep_bits >> (2 * i + 1)) & 1u ? 0xffff0000u : 0u);
-        w[i] &= m;
-    }
-    return __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
-}
-
-// The same masks as a table in constant memory, for keep bits that are
-// wave-uniform: entry b holds the four operand-word masks of mask_pairs(., b),
-// fetched with one scalar load.
-struct alignas(16) PairMaskTable {
-    uint32_t w[256][4];
-};
-constexpr PairMaskTable make_pair_masks()
-{
-    PairMaskTable t{};
-    for (int b = 0; b < 256; ++b)
-        for (int i = 0; i < 4; ++i)
-            t.w[b][i] = (((b >> (2 * i)) & 1) ? 0x0000ffffu : 0u) | (((b >> (2 * i + 1)) & 1) ? 0xffff0000u : 0u);
-    return t;
-}
-__constant__ PairMaskTable kPairMasks = make_pair_masks();
-
-struct WordMask {
-    uint32_t m[4];
-};
-__device__ __forceinline__ WordMask pair_mask(uint64_t keep, int kc)
-{
-    const uint32_t b = (uint32_t)(keep >> (8 * kc)) & 0xffu;
-    const uint4 t = *reinterpret_cast<const uint4 *>(&kPairMasks.w[b][0]);
-    return WordMask{{t.x, t.y, t.z, t.w}};
-}
-__device__ __forceinline__ bf16x8_t apply_mask(bf16x8_t x, const WordMask &m)
-{
-    const uint4 u = __builtin_bit_cast(uint4, x);
-    return __builtin_bit_cast(bf16x8_t, make_uint4(u.x & m.m[0], u.y & m.m[1], u.z & m.m[2], u.w & m.m[3]));
-}
 
 template <int D, bool ROPE, bool CAUSAL, bool WINDOW>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)

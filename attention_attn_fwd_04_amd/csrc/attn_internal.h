@@ -45,10 +45,30 @@ struct RopeArgs {
     int B, Hq, Hkv, S, D;
 };
 
-// Launchers (attn_fwd_kernel.hip, rope_pass.hip).  Return hipSuccess or the
-// launch error.
+// Most splits of one decode: the merge keeps one weight per split in LDS.
+constexpr int kMaxDecodeSplits = 1024;
+
+struct DecodeArgs {
+    const uint16_t *q;        // [B, Hq, D]
+    const uint16_t *k;        // [B, L, Hkv, D] cache
+    const uint16_t *v;
+    uint16_t *o;              // [B, Hq, D]
+    const uint16_t *rope_cs;  // fp16 cos/sin table (positions 0..L-1); null when RoPE is off
+    float *lse;               // [B, Hq] or null
+    float *part_o;            // [B, Hq, n_split, D] partial (unnormalised) outputs
+    float *part_ml;           // [B, Hq, n_split, 2] partial (m, l)
+    int B, Hq, Hkv, L, D;
+    int n_split, keys_per_split;
+    int use_window;
+    float scale_log2e;
+    int32_t window[kMaxPairs];
+};
+
+// Launchers (attn_fwd_kernel.hip, rope_pass.hip, attn_decode.hip).  Return
+// hipSuccess or the launch error.
 hipError_t launch_attn_fwd(const FwdArgs &a, hipStream_t stream);
 hipError_t launch_rope_pass(const RopeArgs &a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
 // Device helpers used by both the fused kernel and the separate RoPE pass, so

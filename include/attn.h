@@ -100,6 +100,43 @@ int attn_fwd_lse(const void *q, const void *k, const void *v, void *o, float *ls
                  const int32_t *window_table, void *stream);
 
 /*
+ * Split-KV decode: one new query per sequence against its KV cache
+ * ("AttnFuse", section 4.2 "Flash Decoding": phase 1 computes, per chunk of
+ * the cache, a partial (m, l, acc) triple with the online-softmax loop;
+ * phase 2 merges the partials through their log-sum-exp).  For every batch b
+ * and query head hq,
+ *
+ *   o[b,hq,:] = sum_{m < L} softmax_m( scale * <R(L-1) q[b,hq,:], k[b,m,hk,:]> ) v[b,m,hk,:]
+ *
+ * with hk = hq / (Hq / Hkv).  The query is the token at position L-1 and is
+ * rotated there when rope_theta > 1 (rope_theta = 0: used as given); the
+ * cache holds keys as they were stored, i.e. already rotated when appended
+ * (attn_rope_apply produces them).  All L keys are visible.
+ *
+ *  q [B,Hq,D], o [B,Hq,D]; k/v [B,L,Hkv,D] (BSHD cache): bf16 device
+ *      pointers, 16-byte aligned; o must not overlap the inputs.
+ *  lse: NULL, or a 4-byte aligned fp32 device array [B,Hq] that receives the
+ *      natural-log log-sum-exp of each head's scaled scores.
+ *  workspace: caller-owned device memory of at least
+ *      attn_decode_workspace_bytes(B, Hq, Hkv, L, D, num_splits) bytes,
+ *      16-byte aligned, for the partial results; its contents on entry do
+ *      not matter.
+ *  Hq / Hkv <= 32 (query heads sharing a KV head go into one MFMA's
+ *      columns); D in {64, 128}; B >= 0, L >= 0 (either 0: no-op).
+ *  window_table: NULL or a HOST array of D/2 non-decreasing int32 limits:
+ *      pair r counts for key m only when (L-1) - m <= w[r] (as in attn_fwd).
+ *  num_splits: 0 lets the library choose (about 1024 waves over the batch,
+ *      at least 64 keys per split); k > 0 asks for k splits (at most one per
+ *      32 keys, at most 1024).  Errors as for attn_fwd.
+ */
+size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int L, int D, int num_splits);
+int attn_decode(const void *q, const void *k, const void *v, void *o, float *lse,
+                void *workspace, size_t workspace_bytes,
+                int B, int Hq, int Hkv, int L, int D,
+                float rope_theta, float scale, const int32_t *window_table,
+                int num_splits, void *stream);
+
+/*
  * The separate RoPE pass ("AttnFuse", section 1 and Figure 1(a): rotate Q
  * and K in their own kernel, then run plain attention): writes the rotated
  * q_out [B,S,Hq,D] and k_out [B,S,Hkv,D] (bf16, rounded to nearest even from

@@ -138,3 +138,52 @@ def _lse_call(lse, S=128):
 ])
 def test_fwd_lse_rejects_bad_lse(lse, status):
     assert _lse_call(lse) == status
+
+
+def test_decode_workspace_bytes():
+    """Partial outputs (fp32 x D) and (m, l) pairs per (b, hq, split): at
+    least one split, at most one per 32 keys; 0 for invalid sizes."""
+    ws = binding.attn_decode_workspace_bytes
+    assert ws(0, 8, 2, 100, 128) == 0 and ws(1, 8, 2, 0, 128) == 0 and ws(1, 8, 2, 10, 128, -1) == 0
+    one = ws(2, 8, 2, 1000, 128, 1)
+    assert one >= 2 * 8 * (128 + 2) * 4
+    assert ws(2, 8, 2, 1000, 128, 4) >= 4 * 2 * 8 * (128 + 2) * 4
+    # at most ceil(1000 / 32) = 32 splits, whatever is asked
+    assert ws(2, 8, 2, 1000, 128, 10 ** 6) == ws(2, 8, 2, 1000, 128, 32)
+    assert ws(1, 64, 8, 32768, 128) > 0
+
+
+def _dec_call(**kw):
+    """attn_decode with fake device addresses: only argument errors caught
+    before any device call are exercised here."""
+    a = dict(q=A, k=A * 64, v=A * 128, o=A * 192, lse=None, ws=A * 256, nws=1 << 30, B=1, Hq=8, Hkv=2,
+             L=100, D=128, theta=1e4, scale=0.088, w=None, ns=0)
+    a.update(kw)
+    return binding.lib().attn_decode(a["q"], a["k"], a["v"], a["o"], a["lse"], a["ws"], a["nws"], a["B"],
+                                     a["Hq"], a["Hkv"], a["L"], a["D"], a["theta"], a["scale"], a["w"],
+                                     a["ns"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Hq=66, Hkv=2), binding.ATTN_EUNSUPPORTED),   # 33 query heads per KV head
+    (dict(D=96), binding.ATTN_EUNSUPPORTED),
+    (dict(Hq=5, Hkv=2), binding.ATTN_EINVAL),
+    (dict(ns=-1), binding.ATTN_EINVAL),
+    (dict(ws=0), binding.ATTN_EINVAL),
+    (dict(q=0), binding.ATTN_EINVAL),
+    (dict(q=A + 8), binding.ATTN_EALIGN),
+    (dict(ws=A * 256 + 4), binding.ATTN_EALIGN),
+    (dict(lse=A * 300 + 2), binding.ATTN_EALIGN),
+    (dict(scale=0.0), binding.ATTN_EINVAL),
+    (dict(theta=0.5), binding.ATTN_EINVAL),
+    (dict(nws=64), binding.ATTN_EINVAL),                 # workspace too small
+    (dict(o=A), binding.ATTN_EINVAL),                    # o aliases q
+    (dict(ws=A * 192), binding.ATTN_EINVAL),             # workspace overlaps o
+])
+def test_decode_rejects(kw, status):
+    assert _dec_call(**kw) == status
+
+
+def test_decode_empty_is_ok_without_device():
+    assert _dec_call(B=0, q=0, k=0, v=0, o=0, ws=0, nws=0) == binding.ATTN_OK
+    assert _dec_call(L=0, q=0, k=0, v=0, o=0, ws=0, nws=0) == binding.ATTN_OK
