@@ -126,11 +126,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
     int work = blockIdx.x;
     if ((n_work & 7) == 0)
         work = (blockIdx.x & 7) * (n_work >> 3) + (blockIdx.x >> 3);
-    const int bh = work / n_qt;
-    const int qt = n_qt - 1 - (work - bh * n_qt);
-    const int b = bh / a.Hq;
+    // (readfirstlane: the divisions run on the vector unit; their results are
+    // wave-uniform, and everything derived from them can then live in scalar
+    // registers, the load descriptors included.)
+    const int bh = __builtin_amdgcn_readfirstlane(work / n_qt);
+    const int qt = __builtin_amdgcn_readfirstlane(n_qt - 1 - (work - bh * n_qt));
+    const int b = __builtin_amdgcn_readfirstlane(bh / a.Hq);
     const int hq = bh - b * a.Hq;
-    const int hk = hq / (a.Hq / a.Hkv);
+    const int hk = __builtin_amdgcn_readfirstlane(hq / (a.Hq / a.Hkv));
     const int n0 = qt * kBM;
     const int S = a.S;
 
@@ -197,13 +200,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
     auto kslot = [&](int t) __attribute__((always_inline)) { return smem + G::KRING + (t & 3) * G::TILE_B; };
     auto vslot = [&](int t) __attribute__((always_inline)) { return smem + G::VRING + (t % 3) * G::TILE_B; };
     auto cslot = [&](int t) __attribute__((always_inline)) { return smem + G::CRING + (t % 3) * G::TILE_B; };
+    // The same slots as 32-bit LDS addresses, for the direct loads.
+    const uint32_t smem32 = lds_addr(smem);
+    auto kslot32 = [&](int t) __attribute__((always_inline)) { return smem32 + (uint32_t)(G::KRING + (t & 3) * G::TILE_B); };
+    auto vslot32 = [&](int t) __attribute__((always_inline)) { return smem32 + (uint32_t)(G::VRING + (t % 3) * G::TILE_B); };
+    auto cslot32 = [&](int t) __attribute__((always_inline)) { return smem32 + (uint32_t)(G::CRING + (t % 3) * G::TILE_B); };
 
     // Direct loads of this wave's share of a tile: instructions wave + 8 i,
     // each 1 KB = RPI rows; lane l writes chunk slot l % CH of row l / CH, i.e.
     // the global chunk (slot ^ swizzle(row)).  Rows are keys (K, V) or
     // positions (the cos/sin table, whose rows have the K row geometry).
     const int dl_row = lane / G::CH, dl_slot = lane % G::CH;
-    auto dload = [&](u32x4_t rs, uint32_t rowb, uint8_t *dst, int t, bool vlayout)
+    auto dload = [&](u32x4_t rs, uint32_t rowb, uint32_t dst, int t, bool vlayout)
         __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < G::NI_W; ++i) {
@@ -211,14 +219,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
             const int r = ins * G::RPI + dl_row;
             const int sw = vlayout ? G::vx(r) : G::kx(r);
             const uint32_t off = (uint32_t)(t * kBN + r) * rowb + 16u * (uint32_t)(dl_slot ^ sw);
-            dma16(rs, off, dst + ins * 1024);
+            dma16(rs, off, dst + (uint32_t)(ins * 1024));
         }
     };
     auto dload_k = [&](int t) __attribute__((always_inline)) {
-        dload(k_rs, kv_rowb, kslot(t), t, false);
-        if constexpr (ROPE) dload(cs_desc, (uint32_t)G::ROWB, cslot(t), t, false);
+        dload(k_rs, kv_rowb, kslot32(t), t, false);
+        if constexpr (ROPE) dload(cs_desc, (uint32_t)G::ROWB, cslot32(t), t, false);
     };
-    auto dload_v = [&](int t) __attribute__((always_inline)) { dload(v_rs, kv_rowb, vslot(t), t, true); };
+    auto dload_v = [&](int t) __attribute__((always_inline)) { dload(v_rs, kv_rowb, vslot32(t), t, true); };
     // Loads of iteration i, one 1 KB instruction per step: V(i+1), K(i+3)
     // and, with RoPE, the cos/sin rows of K(i+3).  They are issued in every
     // iteration: tiles past the end read as zeros into slots that are free
@@ -229,13 +237,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
         const int r = ins * G::RPI + dl_row;
         if (which == 0) {
             const uint32_t off = (uint32_t)((i + 1) * kBN + r) * kv_rowb + 16u * (uint32_t)(dl_slot ^ G::vx(r));
-            dma16(v_rs, off, vslot(i + 1) + ins * 1024);
+            dma16(v_rs, off, vslot32(i + 1) + (uint32_t)(ins * 1024));
         } else if (which == 1) {
             const uint32_t off = (uint32_t)((i + 3) * kBN + r) * kv_rowb + 16u * (uint32_t)(dl_slot ^ G::kx(r));
-            dma16(k_rs, off, kslot(i + 3) + ins * 1024);
+            dma16(k_rs, off, kslot32(i + 3) + (uint32_t)(ins * 1024));
         } else {
             const uint32_t off = (uint32_t)((i + 3) * kBN + r) * (uint32_t)G::ROWB + 16u * (uint32_t)(dl_slot ^ G::kx(r));
-            dma16(cs_desc, off, cslot(i + 3) + ins * 1024);
+            dma16(cs_desc, off, cslot32(i + 3) + (uint32_t)(ins * 1024));
         }
     };
 

@@ -105,6 +105,22 @@ __device__ __forceinline__ void dma16(u32x4_t r, uint32_t voff, const uint8_t *l
                  : "memory", "m0");
 }
 
+// The same with the LDS destination as a 32-bit LDS byte address (no
+// generic-pointer conversion, hence no null check in scalar code).
+__device__ __forceinline__ void dma16(u32x4_t r, uint32_t voff, uint32_t lds_base)
+{
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base);
+    u32x4_t rs;
+    rs.x = __builtin_amdgcn_readfirstlane(r.x);
+    rs.y = __builtin_amdgcn_readfirstlane(r.y);
+    rs.z = __builtin_amdgcn_readfirstlane(r.z);
+    rs.w = __builtin_amdgcn_readfirstlane(r.w);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(rs), "s"(m0)
+                 : "memory", "m0");
+}
+
 // s_waitcnt on the vector-memory counter only: at most n loads of this wave
 // still in flight (loads retire in issue order).
 template <int N>
