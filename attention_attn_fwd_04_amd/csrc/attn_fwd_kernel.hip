@@ -44,11 +44,15 @@
 //  * LDS tiles are XOR-swizzled in 16-byte chunks so the MFMA operand reads,
 //    the transpose reads and the rotation's reads and writes are free of bank
 //    conflicts without padding.
+//  * Scores leave the MFMAs in the exp2 domain, already shifted: Q' is kept
+//    multiplied by c = scale log2 e, and each QK accumulator chain starts
+//    from -m_ref, so P = exp2(accumulator) needs no multiply-add.
 //  * The softmax rescale is lazy: P is computed against the running reference
-//    max m_ref; only when a lane's partial row sum of P exceeds 2^14 (or is
-//    not finite: the first tile) is the tile's true max taken, O and l
-//    rescaled, and P recomputed.  So every P is at most 2^14, the common tile
-//    needs no max pass, and the 64 multiplies of O are rare.
+//    m_ref (set from the wave's first tile); only when a lane's partial row
+//    sum of P exceeds 2^14 (or is not finite) is the tile's max taken, m_ref
+//    raised, O and l rescaled, and P recomputed.  So every P is at most
+//    2^14, the common tile needs no max pass, and the 64 multiplies of O are
+//    rare.
 //  * Key tiles are visited from 0 upwards; the masked tiles are the last
 //    ones.  Query tiles are issued longest first, and the block index is
 //    remapped so one head's tiles run on one XCD (shared L2 for its K/V).
@@ -158,10 +162,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
         const uint32_t n = (uint32_t)(n0 + row);
         uint4 lo = bload16(q_rs, n * q_rowb + 16u * pg);
         uint4 hi = bload16(q_rs, n * q_rowb + (uint32_t)D + 16u * pg);
+        // Q' is kept multiplied by c = scale log2 e (rounded to bf16 once,
+        // after the rotation): the MFMAs then deliver scores in the exp2
+        // domain and P needs no multiply-add.
         if constexpr (ROPE) {
             const uint4 cq = bload16(cs_rs, n * G::ROWB + 16u * pg);
             const uint4 sq = bload16(cs_rs, n * G::ROWB + 16u * (G::PG + pg));
-            rope_rotate8(lo, hi, cq, sq);
+            rope_rotate8_scaled(lo, hi, cq, sq, a.scale_log2e);
+        } else {
+            lo = scale_bf16x8(lo, a.scale_log2e);
+            hi = scale_bf16x8(hi, a.scale_log2e);
         }
         lds_at<uint4>(smem, row * G::QP_B + 16 * pg) = lo;
         lds_at<uint4>(smem, row * G::QP_B + 16 * (G::PG + pg)) = hi;
@@ -280,7 +290,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
     for (int db = 0; db < G::DB; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc_o[db][i] = 0.f;
-    float m_ref = -__builtin_inff(), l_run = 0.f;
+    // Softmax reference in the exp2 domain: every QK MFMA chain starts from
+    // -m_ref in all 16 accumulator entries, so the accumulator holds
+    // s c - m_ref and P is exp2 of it directly.  m_ref is set from the first
+    // tile's max.
+    float m_ref = 0.f, l_run = 0.f;
     f32x16_t sc[2];                        // scores of one tile (S^T, two 32-key blocks)
     bf16x8_t pf_a[kBN / 16], pf_b[kBN / 16];   // P of two consecutive tiles as PV B operands
 
@@ -320,18 +334,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
             }
     };
 
-    // P = 2^(s c - m_ref c) of one (masked) tile, packed into pf; returns the
-    // lane's partial row sum.  m_ref = -inf gives inf / NaN sums, which force
-    // the exact path below.
+    // P = 2^(s c - m_ref) of one (masked) tile (s the accumulator: already
+    // shifted), packed into pf; returns the lane's partial row sum.
     auto exp_tile = [&](const f32x16_t (&s)[2], bf16x8_t (&pf)[kBN / 16]) __attribute__((always_inline)) {
-        const float nmc = -m_ref * c;
         float r0 = 0.f, r1 = 0.f;
 #pragma unroll
         for (int ch = 0; ch < kBN / 16; ++ch) {
             const int kb = ch >> 1, h8 = (ch & 1) * 8;
             float p[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) p[e] = fast_exp2(__builtin_fmaf(s[kb][h8 + e], c, nmc));
+            for (int e = 0; e < 8; ++e) p[e] = fast_exp2(s[kb][h8 + e]);
             uint32_t w[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(p[2 * e], p[2 * e + 1]);
@@ -341,46 +353,41 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
         }
         return r0 + r1;
     };
-    // Exact path: move m_ref to the tile's row max, rescale O and l, redo P.
-    auto rescale_exp_tile = [&](const f32x16_t (&s)[2], bf16x8_t (&pf)[kBN / 16]) __attribute__((always_inline)) {
+    auto tile_max = [&](const f32x16_t (&s)[2]) __attribute__((always_inline)) {
         float mx = s[0][0];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-        mx = max_halves(mx);
-        const float m_new = fmaxf(m_ref, mx);
-        const float alpha = (m_new == m_ref) ? 1.0f : fast_exp2((m_ref - m_new) * c);
+        return max_halves(mx);
+    };
+    // Exact path: move m_ref up by the tile's excess d over it, rescale O and
+    // l by 2^-d, redo P.
+    auto rescale_exp_tile = [&](f32x16_t (&s)[2], bf16x8_t (&pf)[kBN / 16]) __attribute__((always_inline)) {
+        const float d = fmaxf(tile_max(s), 0.f);
+        const float alpha = fast_exp2(-d);
         l_run *= alpha;
 #pragma unroll
         for (int db = 0; db < G::DB; ++db)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc_o[db][i] *= alpha;
-        m_ref = m_new;
+        m_ref += d;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[kb][i] -= d;
         return exp_tile(s, pf);
     };
-
-    // O^T += V^T P^T over the four 16-key chunks of V tile t.
-    auto pv = [&](int t, const bf16x8_t (&pf)[kBN / 16]) __attribute__((always_inline)) {
-        const uint32_t vbase = lds_addr(vslot(t));
-        uint32_t vp[G::DB];
+    // The wave's first tile (m_ref = 0, O = l = 0): m_ref becomes the tile's
+    // row max (0 for padding rows past S, which see no key).
+    auto first_exp_tile = [&](f32x16_t (&s)[2], bf16x8_t (&pf)[kBN / 16]) __attribute__((always_inline)) {
+        const float mx = tile_max(s);
+        m_ref = (mx == -__builtin_inff()) ? 0.f : mx;
 #pragma unroll
-        for (int db = 0; db < G::DB; ++db) {
-            vp[db] = vbase + (uint32_t)v_addr[db];
-            asm("" : "+v"(vp[db]));
-        }
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int ch = 0; ch < kBN / 16; ++ch) {
-#pragma unroll
-            for (int db = 0; db < G::DB; ++db) {
-                const lds_u8_t *p0 = lds_ptr(vp[db]) + 16 * ch * G::ROWB;
-                const i16x4_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)p0);
-                const i16x4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(p0 + 8 * G::ROWB));
-                const uint2 u0 = __builtin_bit_cast(uint2, t0), u1 = __builtin_bit_cast(uint2, t1);
-                const bf16x8_t va = __builtin_bit_cast(bf16x8_t, make_uint4(u0.x, u0.y, u1.x, u1.y));
-                acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[ch], acc_o[db], 0, 0, 0);
-            }
-        }
+            for (int i = 0; i < 16; ++i) s[kb][i] -= m_ref;
+        return exp_tile(s, pf);
     };
 
     // ---- per-pair window ("ATFlash -- Per-RoPE-Wavelength Attention Windows",
@@ -426,6 +433,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
     // K(i+1) spread over the MFMAs (one 32-bit word of each half at a time).
     auto block1 = [&](auto rot_c, int i) __attribute__((always_inline)) {
         constexpr bool ROT = decltype(rot_c)::value;
+        f32x16_t minit;   // -m_ref: the start of both QK chains
+#pragma unroll
+        for (int e = 0; e < 16; ++e) minit[e] = -m_ref;
         const uint32_t kbase = lds_addr(kslot(i));
         uint32_t kp[G::KCH];
 #pragma unroll
@@ -459,7 +469,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
             }
             const int kc = k >> 1, kb = k & 1;
             if (kc == 0) {
-                sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[k], qreg[kc], f32x16_t{}, 0, 0, 0);
+                sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[k], qreg[kc], minit, 0, 0, 0);
             } else {
                 sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[k], qreg[kc], sc[kb], 0, 0, 0);
             }
@@ -497,6 +507,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
         constexpr int C0 = GEN ? 0 : NS;                  // first chunk computed
         constexpr int NM = 2 * (G::KCH - C0);             // MFMAs of this variant
         static_assert(NM >= 4, "rotation words spread over the MFMAs");
+        f32x16_t minit;   // -m_ref: the start of both QK chains
+#pragma unroll
+        for (int e = 0; e < 16; ++e) minit[e] = -m_ref;
         const uint32_t kbase = lds_addr(kslot(i));
         uint32_t kp[G::KCH];
 #pragma unroll
@@ -538,7 +551,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
             bf16x8_t op = kop[k];
             if constexpr (GEN) op = apply_mask(op, pair_mask(wkeep[kb], kc));
             else if (kc < NS + 2) op = apply_mask(op, msk[kb][kc - NS]);
-            sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, qreg[kc], kc == C0 ? f32x16_t{} : sc[kb], 0, 0, 0);
+            sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, qreg[kc], kc == C0 ? minit : sc[kb], 0, 0, 0);
             if constexpr (ROT) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
@@ -560,7 +573,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
     };
 
     // Block 2: O^T += V(i-1)^T P(i-1)^T from pp; with EXP, P(i) = 2^(S(i) c
-    // - m_ref c) into pn, two scores per step, 32 steps spread over the MFMAs.
+    // - m_ref) into pn, two scores per step, 32 steps spread over the MFMAs.
     // Returns the lane's partial row sum of P(i).
     auto block2 = [&](auto exp_c, int i, const bf16x8_t (&pp)[kBN / 16], bf16x8_t (&pn)[kBN / 16])
         __attribute__((always_inline)) {
@@ -579,7 +592,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
             vt0[k] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)p0);
             vt1[k] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(p0 + 8 * G::ROWB));
         };
-        const float nmc = -m_ref * c;
         float r[4] = {0.f, 0.f, 0.f, 0.f};
         uint32_t w[16];
         // Step e: scores 2e, 2e+1 in P order (chunk e / 4, word e % 4).
@@ -587,8 +599,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
         // fence (without it the arithmetic is sunk below the last MFMA).
         auto exp_step = [&](int e) __attribute__((always_inline)) {
             const int ch = e >> 2, kb = ch >> 1, h = (ch & 1) * 8 + 2 * (e & 3);
-            const float p0 = fast_exp2(__builtin_fmaf(sc[kb][h], c, nmc));
-            const float p1 = fast_exp2(__builtin_fmaf(sc[kb][h + 1], c, nmc));
+            const float p0 = fast_exp2(sc[kb][h]);
+            const float p1 = fast_exp2(sc[kb][h + 1]);
             w[e] = pack_bf16x2(p0, p1);
             r[e & 3] = sum_bf16x2(w[e], r[e & 3]);
             asm volatile("" : "+v"(w[e]), "+v"(r[e & 3]));
@@ -734,7 +746,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
         // iteration 0: S(0), P(0) into pf_a
         if constexpr (WINDOW) scores_w(std::false_type{}, 0);
         else scores(0);
-        accept(exp_tile(sc, pf_a), pf_a);
+        l_run = first_exp_tile(sc, pf_a);
         finish(0);
         if constexpr (WINDOW) {
             // One iteration per trip (the window variants make the body
@@ -772,10 +784,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
     if (n >= S) return;
     // Optional log-sum-exp of the row's scaled scores, L = m + log l in the
     // natural-log domain ("AttnFuse", section 4.4: the one value per row the
-    // forward pass keeps for a backward pass): sum_m 2^(s c) = 2^(m_ref c) l.
+    // forward pass keeps for a backward pass): sum_m 2^(s c) = 2^m_ref l.
     if (a.lse != nullptr && g == 0)
         a.lse[((size_t)b * a.Hq + hq) * S + n] =
-            (m_ref * c + __builtin_amdgcn_logf(l_row)) * 0.693147180559945309f;
+            (m_ref + __builtin_amdgcn_logf(l_row)) * 0.693147180559945309f;
     uint16_t *orow = og + (size_t)n * a.Hq * D;
 #pragma unroll
     for (int db = 0; db < G::DB; ++db)

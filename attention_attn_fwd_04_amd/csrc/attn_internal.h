@@ -72,7 +72,8 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
 // Device helpers used by both the fused kernel and the separate RoPE pass, so
-// that both produce the same rotated bf16 bits.
+// that both produce the same rotated bf16 bits (for K; the fused kernel's
+// query is scaled before its one rounding).
 // ---------------------------------------------------------------------------
 #if defined(__HIPCC__)
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -107,6 +108,34 @@ __device__ __forceinline__ void rope_rotate_word(uint32_t &l, uint32_t &h, const
     const float yr1 = __builtin_fmaf(y1, c1, x1 * s1);
     l = pack_bf16x2(xr0, xr1);
     h = pack_bf16x2(yr0, yr1);
+}
+
+// The same rotation with the results multiplied by k before the bf16
+// rounding (one rounding of k x', k y').
+__device__ __forceinline__ void rope_rotate_word_scaled(uint32_t &l, uint32_t &h, const uint32_t cw, const uint32_t sw,
+                                                        const float k)
+{
+    const float x0 = bf16_lo(l), x1 = bf16_hi(l);
+    const float y0 = bf16_lo(h), y1 = bf16_hi(h);
+    const float c0 = half_lo(cw), c1 = half_hi(cw);
+    const float s0 = half_lo(sw), s1 = half_hi(sw);
+    l = pack_bf16x2(__builtin_fmaf(x0, c0, -(y0 * s0)) * k, __builtin_fmaf(x1, c1, -(y1 * s1)) * k);
+    h = pack_bf16x2(__builtin_fmaf(y0, c0, x0 * s0) * k, __builtin_fmaf(y1, c1, x1 * s1) * k);
+}
+
+__device__ __forceinline__ void rope_rotate8_scaled(uint4 &lo, uint4 &hi, const uint4 cq, const uint4 sq, const float k)
+{
+    rope_rotate_word_scaled(lo.x, hi.x, cq.x, sq.x, k);
+    rope_rotate_word_scaled(lo.y, hi.y, cq.y, sq.y, k);
+    rope_rotate_word_scaled(lo.z, hi.z, cq.z, sq.z, k);
+    rope_rotate_word_scaled(lo.w, hi.w, cq.w, sq.w, k);
+}
+
+// bf16 words times k, rounded once.
+__device__ __forceinline__ uint4 scale_bf16x8(const uint4 u, const float k)
+{
+    return make_uint4(pack_bf16x2(bf16_lo(u.x) * k, bf16_hi(u.x) * k), pack_bf16x2(bf16_lo(u.y) * k, bf16_hi(u.y) * k),
+                      pack_bf16x2(bf16_lo(u.z) * k, bf16_hi(u.z) * k), pack_bf16x2(bf16_lo(u.w) * k, bf16_hi(u.w) * k));
 }
 
 __device__ __forceinline__ void rope_rotate8(uint4 &lo, uint4 &hi, const uint4 cq, const uint4 sq)

@@ -140,10 +140,12 @@ int attn_decode(const void *q, const void *k, const void *v, void *o, float *lse
  * The separate RoPE pass ("AttnFuse", section 1 and Figure 1(a): rotate Q
  * and K in their own kernel, then run plain attention): writes the rotated
  * q_out [B,S,Hq,D] and k_out [B,S,Hkv,D] (bf16, rounded to nearest even from
- * the same fp32 arithmetic the fused kernel uses, so that
- * attn_rope_apply + attn_fwd(rope_theta = 0) reproduces attn_fwd with RoPE
- * bit for bit).  q_out/k_out are caller-owned workspaces that must not
- * overlap the inputs.  rope_theta must be > 1.
+ * the same fp32 arithmetic the fused kernel uses: the rotated keys are the
+ * fused kernel's bit for bit; the fused kernel rounds the rotated query once
+ * after scaling it by scale * log2 e, attn_fwd(rope_theta = 0) on q_out
+ * rounds it a second time, so the two paths agree to that rounding).
+ * q_out/k_out are caller-owned workspaces that must not overlap the inputs.
+ * rope_theta must be > 1.
  */
 int attn_rope_apply(const void *q, const void *k, void *q_out, void *k_out,
                     int B, int Hq, int Hkv, int S, int D, float rope_theta,

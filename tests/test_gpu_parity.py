@@ -1,9 +1,10 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
 
 Tolerance for bf16 outputs: max |err| <= 2e-2 and mean |err| <= 2e-3 over
-the compared elements.  Bitwise gates: fused RoPE == separate RoPE pass +
-plain attention, window with every pair kept == no window, causal row 0 ==
-V[0], and run-to-run determinism.
+the compared elements.  Bitwise gates: window with every pair kept == no
+window, causal row 0 == V[0], and run-to-run determinism.  The separate
+path (RoPE pass + plain attention) meets the same bar; it rounds the
+rotated query once more than the fused kernel.
 """
 import math
 
@@ -94,12 +95,17 @@ def test_fused_matches_oracle(B, Hq, Hkv, S, D, theta, causal):
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,S,D,theta,causal", [c for c in CASES if c[5] > 0])
-def test_separate_pass_is_bitwise_fused(B, Hq, Hkv, S, D, theta, causal):
+def test_separate_pass_matches_oracle_and_fused(B, Hq, Hkv, S, D, theta, causal):
+    """The separate path (rope pass, then attention without RoPE) meets the
+    bar against the oracle.  Its K' is the fused kernel's bit for bit; its Q'
+    is rounded twice (pass output, then times scale log2 e) where the fused
+    kernel rounds once, so the two outputs agree to that rounding."""
     q, k, v = make_qkv(B, S, Hq, Hkv, D, seed=2000 + S)
     scale = 1 / math.sqrt(D)
     a = run_fused(q, k, v, theta, causal, scale)
     b = run_separate(q, k, v, theta, causal, scale)
-    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert_parity(b, full_ref(q, k, v, theta, causal, scale), label="separate %s" % ((B, Hq, Hkv, S, D, theta, causal),))
+    assert float((a.float() - b.float()).abs().max()) <= MAX_TOL
 
 
 def test_rope_pass_matches_oracle_rotation():
@@ -184,7 +190,7 @@ def test_window_dense_partial_pairs():
     o = run_fused(q, k, v, 1e4, True, scale, window=w)
     assert_parity(o, full_ref(q, k, v, 1e4, True, scale, w), label="window dense")
     o2 = run_separate(q, k, v, 1e4, True, scale, window=w)
-    assert torch.equal(o.view(torch.int16), o2.view(torch.int16))
+    assert_parity(o2, full_ref(q, k, v, 1e4, True, scale, w), label="window dense, separate")
 
 
 def test_window_all_kept_is_bitwise_no_window():
