@@ -28,8 +28,9 @@
 //    the same table and routine as the other kernels.
 //  * With a per-pair window ("ATFlash -- Per-RoPE-Wavelength Attention
 //    Windows", "The idea") the query's pairs are masked per tile: pairs
-//    pruned on the whole tile drop out of the MFMA, pairs whose limit falls
-//    inside the tile are added back one MFMA each where n - m <= w[r].
+//    pruned on the whole tile drop out of the MFMA (and their K columns are
+//    not fetched), pairs whose limit falls inside the tile are added back
+//    one MFMA each where n - m <= w[r].
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -115,13 +116,29 @@ __global__ __launch_bounds__(kDecWaves * 64, 1) void decode_split_kernel(const D
     auto kslot = [&](int t) { return ring + (t & 1) * (2 * G::TILE_B); };
     auto vslot = [&](int t) { return ring + (t & 1) * (2 * G::TILE_B) + G::TILE_B; };
     const int dl_row = lane / G::CH, dl_slot = lane % G::CH;
+    // Window: lane r holds w[r] (pairs past D/2: never pruned).
+    typedef __attribute__((address_space(4))) const int32_t kconst_i32;
+    kconst_i32 *wtab = (kconst_i32 *)((__attribute__((address_space(4))) const char *)
+                                          __builtin_amdgcn_kernarg_segment_ptr() + __builtin_offsetof(DecodeArgs, window));
+    const int w_lane = (WINDOW && lane < D / 2) ? wtab[lane] : INT_MAX;
+
+    // With a window, the K columns of an 8-pair group pruned on the whole
+    // tile are not fetched ("ATFlash", the out-of-window prefix never enters
+    // on-chip memory): their lanes get an offset past the buffer, which
+    // loads zeros without a memory access.
     auto load_tile = [&](int t) __attribute__((always_inline)) {
         const int m0 = m_begin + t * kDecBN;
+        uint64_t gpr = 0;   // pairs pruned on the whole tile
+        if constexpr (WINDOW) gpr = __builtin_amdgcn_ballot_w64(w_lane < max(0, pos - (m0 + kDecBN - 1)));
 #pragma unroll
         for (int ins = 0; ins < G::NI; ++ins) {
             const int r = ins * G::RPI + dl_row;
             const uint32_t row = (uint32_t)(m0 + r) * kv_rowb;
-            dma16(k_rs, row + 16u * (uint32_t)(dl_slot ^ G::kx(r)), kslot(t) + ins * 1024);
+            const int kc = dl_slot ^ G::kx(r);   // chunk of the row: pair group kc % PG
+            uint32_t koff = row + 16u * (uint32_t)kc;
+            if constexpr (WINDOW)
+                if (((gpr >> (8 * (kc % G::PG))) & 0xffu) == 0xffu) koff = 0x80000000u;
+            dma16(k_rs, koff, kslot(t) + ins * 1024);
             dma16(v_rs, row + 16u * (uint32_t)(dl_slot ^ G::vx(r)), vslot(t) + ins * 1024);
         }
     };
@@ -135,12 +152,6 @@ __global__ __launch_bounds__(kDecWaves * 64, 1) void decode_split_kernel(const D
 #pragma unroll
     for (int db = 0; db < G::DB; ++db)
         v_addr[db] = G::v_off(4 * g + tr_key, (32 * db + tr_dim) >> 3) + 2 * (tr_dim & 4);
-
-    // Window: lane r holds w[r] (pairs past D/2: never pruned).
-    typedef __attribute__((address_space(4))) const int32_t kconst_i32;
-    kconst_i32 *wtab = (kconst_i32 *)((__attribute__((address_space(4))) const char *)
-                                          __builtin_amdgcn_kernarg_segment_ptr() + __builtin_offsetof(DecodeArgs, window));
-    const int w_lane = (WINDOW && lane < D / 2) ? wtab[lane] : INT_MAX;
 
     f32x16_t acc_o[G::DB];
 #pragma unroll
