@@ -268,6 +268,140 @@ int oracle_decode(const uint16_t *q, const uint16_t *k, const uint16_t *v,
     return 0;
 }
 
+/* Inverse rotation (by -angle) of one fp64 row, in place. */
+static void unrotate_row(double *x, int D, double theta, double pos)
+{
+    int half = D / 2;
+    if (theta == 0.0)
+        return;
+    for (int r = 0; r < half; ++r) {
+        double freq = pow(theta, -2.0 * (double)r / (double)D);
+        double ang = pos * freq;
+        double c = cos(ang), s = sin(ang);
+        double a = x[r], b = x[r + half];
+        x[r] = a * c + b * s;
+        x[r + half] = b * c - a * s;
+    }
+}
+
+/*
+ * Backward of the attention above ("AttnFuse", section 4.4 "Backward Pass":
+ * the gradients with respect to Q, K and V), from the plain definition:
+ *   P = softmax(S), S = scale Q'K'^T (masked), O = P V, upstream dO:
+ *   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - rowsum(P o dP)),
+ *   dQ' = scale dS K',  dK' = scale dS^T Q',
+ * then dQ = R(n)^T dQ' and dK = R(m)^T dK' (the rotation is orthogonal).
+ * With grouped heads, dK and dV of a KV head sum over its query heads.
+ * q, do: [B,S,Hq,D]; k, v: [B,S,Hkv,D] bf16 bits; dq [B,S,Hq,D],
+ * dk, dv [B,S,Hkv,D] fp64 outputs.  No window.
+ */
+int oracle_attn_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                    const uint16_t *dout, int B, int S, int Hq, int Hkv, int D,
+                    double rope_theta, int causal, double scale, double *dq,
+                    double *dk, double *dv)
+{
+    if (B < 0 || S < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || D > 1024 ||
+        (D % 2) != 0 || (Hq % Hkv) != 0)
+        return -1;
+    int group = Hq / Hkv;
+    size_t nq = (size_t)B * S * Hq * D, nkv = (size_t)B * S * Hkv * D;
+    memset(dq, 0, sizeof(double) * nq);
+    memset(dk, 0, sizeof(double) * nkv);
+    memset(dv, 0, sizeof(double) * nkv);
+    for (int b = 0; b < B; ++b) {
+        for (int hk = 0; hk < Hkv; ++hk) {
+            double *kr = rotated_keys(k, S, Hkv, D, b, hk, rope_theta, 0);
+            double *dkr = (double *)calloc((size_t)S * D, sizeof(double));
+            if (!kr || !dkr) {
+                free(kr);
+                free(dkr);
+                return -1;
+            }
+            for (int g = 0; g < group; ++g) {
+                int hq = hk * group + g;
+#pragma omp parallel
+                {
+                    double *dkr_t = (double *)calloc((size_t)S * D, sizeof(double));
+                    double *dv_t = (double *)calloc((size_t)S * D, sizeof(double));
+                    double *p = (double *)malloc(sizeof(double) * (size_t)(S > 0 ? S : 1));
+                    double *dp = (double *)malloc(sizeof(double) * (size_t)(S > 0 ? S : 1));
+#pragma omp for schedule(dynamic, 4)
+                    for (int n = 0; n < S; ++n) {
+                        double qraw[1024], qr[1024], dor[1024], dqr[1024];
+                        const uint16_t *qs = row_ptr(q, S, Hq, D, b, n, hq);
+                        const uint16_t *ds = row_ptr(dout, S, Hq, D, b, n, hq);
+                        for (int d = 0; d < D; ++d) {
+                            qraw[d] = widen_bf16(qs[d]);
+                            dor[d] = widen_bf16(ds[d]);
+                            dqr[d] = 0.0;
+                        }
+                        rotate_row(qraw, D, rope_theta, (double)n, qr);
+                        int m_end = causal ? n + 1 : S;
+                        double mu = -INFINITY;
+                        for (int m = 0; m < m_end; ++m) {
+                            p[m] = score(qr, kr + (size_t)m * D, D, scale, NULL, 0);
+                            if (p[m] > mu)
+                                mu = p[m];
+                        }
+                        double z = 0.0;
+                        for (int m = 0; m < m_end; ++m) {
+                            p[m] = exp(p[m] - mu);
+                            z += p[m];
+                        }
+                        double delta = 0.0;
+                        for (int m = 0; m < m_end; ++m) {
+                            p[m] /= z;
+                            const uint16_t *vs = row_ptr(v, S, Hkv, D, b, m, hk);
+                            double acc = 0.0;
+                            for (int d = 0; d < D; ++d)
+                                acc += dor[d] * widen_bf16(vs[d]);
+                            dp[m] = acc;
+                            delta += p[m] * acc;
+                        }
+                        for (int m = 0; m < m_end; ++m) {
+                            double dsm = p[m] * (dp[m] - delta);
+                            const double *km = kr + (size_t)m * D;
+                            double *dkm = dkr_t + (size_t)m * D, *dvm = dv_t + (size_t)m * D;
+                            for (int d = 0; d < D; ++d) {
+                                dqr[d] += scale * dsm * km[d];
+                                dkm[d] += scale * dsm * qr[d];
+                                dvm[d] += p[m] * dor[d];
+                            }
+                        }
+                        unrotate_row(dqr, D, rope_theta, (double)n);
+                        double *dqo = dq + (((size_t)b * S + n) * Hq + hq) * (size_t)D;
+                        for (int d = 0; d < D; ++d)
+                            dqo[d] = dqr[d];
+                    }
+#pragma omp critical
+                    {
+                        for (size_t i = 0; i < (size_t)S * D; ++i)
+                            dkr[i] += dkr_t[i];
+                        for (int m = 0; m < S; ++m) {
+                            double *dvo = dv + (((size_t)b * S + m) * Hkv + hk) * (size_t)D;
+                            for (int d = 0; d < D; ++d)
+                                dvo[d] += dv_t[(size_t)m * D + d];
+                        }
+                    }
+                    free(dkr_t);
+                    free(dv_t);
+                    free(p);
+                    free(dp);
+                }
+            }
+            for (int m = 0; m < S; ++m) {
+                unrotate_row(dkr + (size_t)m * D, D, rope_theta, (double)m);
+                double *dko = dk + (((size_t)b * S + m) * Hkv + hk) * (size_t)D;
+                for (int d = 0; d < D; ++d)
+                    dko[d] = dkr[(size_t)m * D + d];
+            }
+            free(kr);
+            free(dkr);
+        }
+    }
+    return 0;
+}
+
 /*
  * The scaled score row s(n, m) for m = 0..S-1 of one query (b, n, hq), with
  * masked keys (m > n under the causal mask) set to -inf.  Used by the

@@ -53,6 +53,10 @@ def _load():
                                   ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_double,
                                   i32p, ctypes.c_longlong, f64p, f64p]
     lib.oracle_decode.restype = ctypes.c_int
+    lib.oracle_attn_bwd.argtypes = [u16p, u16p, u16p, u16p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_int, ctypes.c_double,
+                                    f64p, f64p, f64p]
+    lib.oracle_attn_bwd.restype = ctypes.c_int
     lib.oracle_scores_row.argtypes = [u16p, u16p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                       ctypes.c_int, ctypes.c_int, ctypes.c_double,
                                       ctypes.c_int, ctypes.c_double, i32p,
@@ -131,6 +135,25 @@ def decode(q, k, v, rope_theta, scale, window=None, pos_offset=0, want_lse=False
     if rc != 0:
         raise ValueError("oracle_decode rejected its arguments")
     return (out, lse) if want_lse else out
+
+
+def attn_bwd(q, k, v, do, rope_theta, causal, scale):
+    """Gradients (fp64) of the attention with respect to q, k, v for the
+    upstream gradient do (uint16 bf16 bits, [B,S,Hq,D]).  Returns dq, dk, dv."""
+    lib = _load()
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    assert k.shape == (B, S, Hkv, D) and v.shape == k.shape and do.shape == q.shape
+    q, k, v, do = (np.ascontiguousarray(t) for t in (q, k, v, do))
+    dq = np.zeros(q.shape, dtype=np.float64)
+    dk = np.zeros(k.shape, dtype=np.float64)
+    dv = np.zeros(k.shape, dtype=np.float64)
+    f = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+    rc = lib.oracle_attn_bwd(_u16(q), _u16(k), _u16(v), _u16(do), B, S, Hq, Hkv, D, float(rope_theta),
+                             int(bool(causal)), float(scale), f(dq), f(dk), f(dv))
+    if rc != 0:
+        raise ValueError("oracle_attn_bwd rejected its arguments")
+    return dq, dk, dv
 
 
 def all_rows(B, S, Hq):

@@ -458,3 +458,91 @@ def test_decode_window_matches_brute_force():
     p = np.exp(s - s.max())
     ref = (p / p.sum()) @ _f64(v)[0, :, 0]
     np.testing.assert_allclose(O.decode(q, k, v, 1e4, 0.3, window)[0, 0], ref, rtol=0, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# Backward ("AttnFuse", section 4.4): dQ, dK, dV of the attention above.
+# --------------------------------------------------------------------------
+def _torch_grads(q, k, v, do, theta, causal, scale):
+    """Library special case: torch fp64 autograd through the transformers
+    rotation and scaled_dot_product_attention."""
+    from transformers.models.llama.modeling_llama import apply_rotary_pos_emb
+    B, S, Hq, D = q.shape
+    qt = torch.from_numpy(_f64(q)).permute(0, 2, 1, 3).contiguous().requires_grad_(True)
+    kt = torch.from_numpy(_f64(k)).permute(0, 2, 1, 3).contiguous().requires_grad_(True)
+    vt = torch.from_numpy(_f64(v)).permute(0, 2, 1, 3).contiguous().requires_grad_(True)
+    qr, kr = qt, kt
+    if theta:
+        inv = 1.0 / (theta ** (torch.arange(0, D, 2, dtype=torch.float64) / D))
+        fr = torch.arange(S, dtype=torch.float64)[:, None] * inv[None, :]
+        emb = torch.cat([fr, fr], -1)
+        qr, kr = apply_rotary_pos_emb(qt, kt, emb.cos()[None], emb.sin()[None], unsqueeze_dim=1)
+    o = torch.nn.functional.scaled_dot_product_attention(qr, kr, vt, is_causal=bool(causal), scale=scale,
+                                                         enable_gqa=(Hq != k.shape[2]))
+    o.backward(torch.from_numpy(_f64(do)).permute(0, 2, 1, 3))
+    return tuple(t.grad.permute(0, 2, 1, 3).numpy() for t in (qt, kt, vt))
+
+
+@pytest.mark.parametrize("B,S,Hq,Hkv,D,theta,causal", [
+    (1, 40, 2, 2, 64, 1e4, True),
+    (2, 23, 4, 2, 64, 5e5, True),
+    (1, 31, 4, 1, 128, 1e4, False),
+    (1, 20, 2, 2, 64, 0.0, True),
+])
+def test_bwd_matches_torch_autograd_fp64(B, S, Hq, Hkv, D, theta, causal):
+    q, k, v = _qkv_np(B, S, Hq, Hkv, D, seed=500 + S)
+    do = _qkv_np(B, S, Hq, Hkv, D, seed=600 + S)[0]
+    scale = 1 / math.sqrt(D)
+    ours = O.attn_bwd(q, k, v, do, theta, causal, scale)
+    ref = _torch_grads(q, k, v, do, theta, causal, scale)
+    for name, a, r in zip(("dq", "dk", "dv"), ours, ref):
+        np.testing.assert_allclose(a, r, rtol=0, atol=1e-11, err_msg=name)
+
+
+def test_bwd_matches_finite_differences():
+    """Central differences of <O, dO> with respect to single entries of q,
+    k and v, O from the oracle's forward (step 1e-6 on fp64 inputs is not
+    representable in bf16, so the differences run on a tiny fp64 forward
+    written here from the definition: rotation, scores, softmax, PV)."""
+    B, S, H, D, theta, scale = 1, 6, 1, 4, 100.0, 0.7
+    q, k, v = _qkv_np(B, S, H, H, D, seed=61)
+    do = _qkv_np(B, S, H, H, D, seed=62)[0]
+    qf, kf, vf, dof = (_f64(t)[0, :, 0] for t in (q, k, v, do))
+
+    def loss(qx, kx, vx):
+        qr = brute.rotate(qx, theta, np.arange(S))
+        kr = brute.rotate(kx, theta, np.arange(S))
+        s = scale * qr @ kr.T
+        s = np.where(np.tril(np.ones((S, S), dtype=bool)), s, -np.inf)
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        return float(((p @ vx) * dof).sum())
+
+    dq, dk, dv = (g[0, :, 0] for g in O.attn_bwd(q, k, v, do, theta, True, scale))
+    h = 1e-6
+    for grad, which in ((dq, 0), (dk, 1), (dv, 2)):
+        for (n, d) in ((0, 0), (3, 1), (5, 3), (2, 2)):
+            args = [qf.copy(), kf.copy(), vf.copy()]
+            args[which][n, d] += h
+            up = loss(*args)
+            args[which][n, d] -= 2 * h
+            dn = loss(*args)
+            assert abs((up - dn) / (2 * h) - grad[n, d]) <= 1e-7, (which, n, d)
+
+
+def test_bwd_closed_forms():
+    """dV sums P^T dO: with Q = 0 every causal row is uniform over its keys,
+    so dv[m] = sum_{n >= m} do[n] / (n + 1); and sum over m of dk is 0 with
+    RoPE off (the softmax is shift invariant: sum_m dS[n, m] = 0)."""
+    B, S, H, D = 1, 12, 1, 64
+    _, k, v = _qkv_np(B, S, H, H, D, seed=71)
+    do = _qkv_np(B, S, H, H, D, seed=72)[0]
+    zq = np.zeros_like(do)
+    _, dk, dv = O.attn_bwd(zq, k, v, do, 0.0, True, 0.125)
+    dof = _f64(do)[0, :, 0]
+    ref = np.array([sum(dof[n] / (n + 1) for n in range(m, S)) for m in range(S)])
+    np.testing.assert_allclose(dv[0, :, 0], ref, rtol=0, atol=1e-13)
+    q = _qkv_np(B, S, H, H, D, seed=73)[0]
+    _, dk2, _ = O.attn_bwd(q, k, v, do, 0.0, True, 0.125)
+    # sum over keys of dk'[m] = scale * sum_n q'[n] * sum_m dS[n, m] = 0
+    np.testing.assert_allclose(dk2[0, :, 0].sum(axis=0), 0.0, atol=1e-12)
