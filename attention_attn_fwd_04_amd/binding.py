@@ -24,7 +24,8 @@ ATTN_ENOMEM = -4
 ATTN_ELAUNCH = -5
 ATTN_ENODEVICE = -6
 
-EXPORTED = ("attn_fwd", "attn_fwd_lse", "attn_decode", "attn_decode_workspace_bytes", "attn_rope_apply", "attn_window_table", "attn_pruned_terms",
+EXPORTED = ("attn_fwd", "attn_fwd_lse", "attn_decode", "attn_decode_workspace_bytes", "attn_bwd",
+            "attn_bwd_workspace_bytes", "attn_rope_apply", "attn_window_table", "attn_pruned_terms",
             "attn_check_args", "attn_strerror", "attn_release")
 
 _lib = None
@@ -55,6 +56,10 @@ def lib():
     L.attn_decode.restype = i
     L.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i, i]
     L.attn_decode_workspace_bytes.restype = ctypes.c_size_t
+    L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i, i, i, i, i, f, i, f, i32p, vp]
+    L.attn_bwd.restype = i
+    L.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
+    L.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     L.attn_rope_apply.argtypes = [vp, vp, vp, vp, i, i, i, i, i, f, vp]
     L.attn_rope_apply.restype = i
     L.attn_window_table.argtypes = [d, i, d, i32p]
@@ -201,6 +206,48 @@ def attn_decode(q, k, v, o=None, lse=None, workspace=None, *, rope_theta=10000.0
     if st != ATTN_OK:
         raise AttnError(st, "attn_decode")
     return (o, lse) if lse is not None else o
+
+
+def attn_bwd_workspace_bytes(B, Hq, Hkv, S, D) -> int:
+    return int(lib().attn_bwd_workspace_bytes(int(B), int(Hq), int(Hkv), int(S), int(D)))
+
+
+def attn_bwd(q, k, v, o, lse, dout, dq=None, dk=None, dv=None, workspace=None, *, rope_theta=10000.0,
+             causal=True, scale=None, window_table=None, stream=None):
+    """Attention backward: (dq, dk, dv) for the forward output o and its lse
+    (attn_fwd_lse with the same arguments) and the output gradient dout."""
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        _check_tensor(t, n)
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if k.shape != (B, S, Hkv, D) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, S, Hkv, D] matching q")
+    if o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("o and dout must be shaped like q")
+    if (not isinstance(lse, torch.Tensor) or lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, S)
+            or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 tensor [B, Hq, S]")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for t, n, ref in ((dq, "dq", q), (dk, "dk", k), (dv, "dv", v)):
+        _check_tensor(t, n)
+        if t.shape != ref.shape:
+            raise ValueError("%s must be shaped like %s" % (n, "q" if ref is q else "k"))
+    nbytes = attn_bwd_workspace_bytes(B, Hq, Hkv, S, D)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    w, wp = _window_ptr(window_table, D)
+    st = lib().attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+                        workspace.numel() * workspace.element_size(), B, Hq, Hkv, S, D, float(rope_theta),
+                        1 if causal else 0, float(scale), wp, _stream_handle(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_bwd")
+    return dq, dk, dv
 
 
 def attn_rope_apply(q, k, q_out=None, k_out=None, *, rope_theta=10000.0, stream=None):

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_NAME = "libattn_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["attn_api.cpp", "attn_fwd_kernel.hip", "rope_pass.hip", "attn_decode.hip"]
+SOURCES = ["attn_api.cpp", "attn_fwd_kernel.hip", "rope_pass.hip", "attn_decode.hip", "attn_bwd.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -349,6 +349,84 @@ int attn_decode(const void *q, const void *k, const void *v, void *o, float *lse
     return ATTN_OK;
 }
 
+// Workspace of attn_bwd: the staged queries, the staged keys, then Delta,
+// each section 256-byte aligned.
+size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D)
+{
+    if (B <= 0 || S <= 0 || Hq < 1 || Hkv < 1 || D <= 0) return 0;
+    const size_t qs = ((size_t)B * S * Hq * D * 2 + 255) / 256 * 256;
+    const size_t kr = ((size_t)B * S * Hkv * D * 2 + 255) / 256 * 256;
+    return qs + kr + (size_t)B * Hq * S * 4;
+}
+
+int attn_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout, const float *lse,
+             void *dq, void *dk, void *dv, void *workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int S,
+             int D, float rope_theta, int causal, float scale, const int32_t *window_table, void *stream)
+{
+    int st = check_shapes(B, Hq, Hkv, S, D);
+    if (st != ATTN_OK) return st;
+    if (B > 65535) return ATTN_EUNSUPPORTED;   // grid z
+    if (window_table != nullptr) return ATTN_EUNSUPPORTED;
+    if (causal != 0 && causal != 1) return ATTN_EINVAL;
+    if (!std::isfinite(scale) || !(scale > 0.0f)) return ATTN_EINVAL;
+    st = check_theta(rope_theta);
+    if (st != ATTN_OK) return st;
+    const bool empty = (B == 0 || S == 0);
+    if (!empty && (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace)) return ATTN_EINVAL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
+        !aligned16(dk) || !aligned16(dv) || !aligned16(workspace))
+        return ATTN_EALIGN;
+    if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return ATTN_EALIGN;
+    if (empty) return ATTN_OK;
+    const size_t nws = attn_bwd_workspace_bytes(B, Hq, Hkv, S, D);
+    if (workspace_bytes < nws) return ATTN_EINVAL;
+    const size_t nq = (size_t)B * S * Hq * D * 2, nkv = (size_t)B * S * Hkv * D * 2, nl = (size_t)B * Hq * S * 4;
+    // Every written buffer is disjoint from every other buffer.
+    const void *ins[6] = {q, k, v, o, dout, lse};
+    const size_t in_n[6] = {nq, nkv, nkv, nq, nq, nl};
+    void *outs[4] = {dq, dk, dv, workspace};
+    const size_t out_n[4] = {nq, nkv, nkv, nws};
+    for (int i = 0; i < 4; ++i) {
+        for (int j = 0; j < 6; ++j)
+            if (overlaps(outs[i], out_n[i], ins[j], in_n[j])) return ATTN_EINVAL;
+        for (int j = i + 1; j < 4; ++j)
+            if (overlaps(outs[i], out_n[i], outs[j], out_n[j])) return ATTN_EINVAL;
+    }
+    int dev = -1;
+    st = current_device_ok(&dev);
+    if (st != ATTN_OK) return st;
+
+    attn::BwdArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.q = static_cast<const uint16_t *>(q);
+    a.k = static_cast<const uint16_t *>(k);
+    a.v = static_cast<const uint16_t *>(v);
+    a.o = static_cast<const uint16_t *>(o);
+    a.dout = static_cast<const uint16_t *>(dout);
+    a.lse = lse;
+    a.dq = static_cast<uint16_t *>(dq);
+    a.dk = static_cast<uint16_t *>(dk);
+    a.dv = static_cast<uint16_t *>(dv);
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    const size_t qs_b = (nq + 255) / 256 * 256, kr_b = (nkv + 255) / 256 * 256;
+    a.qs = reinterpret_cast<uint16_t *>(ws);
+    a.kr = reinterpret_cast<uint16_t *>(ws + qs_b);
+    a.delta = reinterpret_cast<float *>(ws + qs_b + kr_b);
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.S = S; a.D = D;
+    a.causal = causal;
+    a.scale = scale;
+    a.scale_log2e = (float)((double)scale * 1.4426950408889634073599246810019);
+    if (rope_theta != 0.0f) {
+        st = get_table(dev, D, rope_theta, S, &a.rope_cs);
+        if (st != ATTN_OK) return st;
+        a.kop = a.kr;
+    } else {
+        a.kop = a.k;
+    }
+    if (attn::launch_attn_bwd(a, static_cast<hipStream_t>(stream)) != hipSuccess) return ATTN_ELAUNCH;
+    return ATTN_OK;
+}
+
 int attn_rope_apply(const void *q, const void *k, void *q_out, void *k_out, int B, int Hq, int Hkv, int S,
                     int D, float rope_theta, void *stream)
 {

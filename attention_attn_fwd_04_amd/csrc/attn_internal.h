@@ -1,5 +1,5 @@
 // attn_internal.h -- declarations shared by the host API (attn_api.cpp) and
-// the gfx950 kernels (attn_fwd_kernel.hip, rope_pass.hip).  Not installed.
+// the gfx950 kernels.  Not installed.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -64,11 +64,33 @@ struct DecodeArgs {
     int32_t window[kMaxPairs];
 };
 
-// Launchers (attn_fwd_kernel.hip, rope_pass.hip, attn_decode.hip).  Return
-// hipSuccess or the launch error.
+struct BwdArgs {
+    const uint16_t *q;        // [B, S, Hq, D]
+    const uint16_t *k;        // [B, S, Hkv, D]
+    const uint16_t *v;
+    const uint16_t *o;        // forward output [B, S, Hq, D]
+    const uint16_t *dout;     // dL/dO [B, S, Hq, D]
+    const float *lse;         // [B, Hq, S] natural-log LSE of the forward's rows
+    uint16_t *dq;             // [B, S, Hq, D]
+    uint16_t *dk;             // [B, S, Hkv, D]
+    uint16_t *dv;
+    uint16_t *qs;             // workspace [B, S, Hq, D]: bf16(scale log2e R(n) q)
+    uint16_t *kr;             // workspace [B, S, Hkv, D]: bf16(R(m) k); unused without RoPE
+    const uint16_t *kop;      // the K operand: kr with RoPE, k without
+    float *delta;             // workspace [B, Hq, S]: rowsum(dO o O)
+    const uint16_t *rope_cs;  // fp16 cos/sin table; null when RoPE is off
+    int B, Hq, Hkv, S, D;
+    int causal;
+    float scale;
+    float scale_log2e;
+};
+
+// Launchers (attn_fwd_kernel.hip, rope_pass.hip, attn_decode.hip,
+// attn_bwd.hip).  Return hipSuccess or the launch error.
 hipError_t launch_attn_fwd(const FwdArgs &a, hipStream_t stream);
 hipError_t launch_rope_pass(const RopeArgs &a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_attn_bwd(const BwdArgs &a, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
 // Device helpers used by both the fused kernel and the separate RoPE pass, so

@@ -137,6 +137,43 @@ int attn_decode(const void *q, const void *k, const void *v, void *o, float *lse
                 int num_splits, void *stream);
 
 /*
+ * Attention backward: the gradients of the attn_fwd loss with respect to q,
+ * k and v, given dout = dL/do ("AttnFuse", section 4.4 "Backward Pass": a
+ * preprocessing kernel for the row-reduced Delta = rowsum(dout o o), one
+ * kernel per key tile for dK and dV, one per query tile for dQ, each writing
+ * its own tile, with the softmax probabilities rebuilt from the saved
+ * per-row lse).  With S(n,m) = scale <R(n) q_n, R(m) k_m> and
+ * P = softmax over the visible m:
+ *
+ *   dv_m = sum_n P(n,m) dout_n
+ *   dS(n,m) = P(n,m) (<dout_n, v_m> - Delta_n)
+ *   dq_n = scale R(n)^T sum_m dS(n,m) R(m) k_m
+ *   dk_m = scale R(m)^T sum_n dS(n,m) R(n) q_n
+ *
+ * summed over the query heads of a group for dk and dv.
+ *
+ *  q, k, v, o, dout: bf16 [B,S,H,D] as for attn_fwd; o is the forward's
+ *      output and lse [B,Hq,S] (fp32, 4-byte aligned) the one attn_fwd_lse
+ *      wrote for the same inputs and arguments.
+ *  dq [B,S,Hq,D], dk, dv [B,S,Hkv,D]: bf16 outputs, overwritten (not
+ *      accumulated into); they must not overlap each other, the inputs or the
+ *      workspace.
+ *  workspace: caller-owned device memory of at least
+ *      attn_bwd_workspace_bytes(B, Hq, Hkv, S, D) bytes, 16-byte aligned
+ *      (staged operands and Delta); contents on entry do not matter.
+ *  window_table must be NULL (the backward of the per-pair window is not
+ *      built: ATTN_EUNSUPPORTED).  B <= 65535.  Other arguments and errors as
+ *      for attn_fwd.
+ */
+size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D);
+int attn_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
+             const float *lse, void *dq, void *dk, void *dv,
+             void *workspace, size_t workspace_bytes,
+             int B, int Hq, int Hkv, int S, int D,
+             float rope_theta, int causal, float scale,
+             const int32_t *window_table, void *stream);
+
+/*
  * The separate RoPE pass ("AttnFuse", section 1 and Figure 1(a): rotate Q
  * and K in their own kernel, then run plain attention): writes the rotated
  * q_out [B,S,Hq,D] and k_out [B,S,Hkv,D] (bf16, rounded to nearest even from

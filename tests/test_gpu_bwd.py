@@ -1,0 +1,126 @@
+"""GPU parity of attn_bwd (through the C ABI) against the fp64 oracle.
+
+The forward output o and its lse come from attn_fwd_lse on the GPU, as in
+training; the oracle recomputes everything from q, k, v and dout in fp64.
+
+Tolerance.  The pages verify gradients against a plain reference with FA2's
+fp16 bar, |err| < 2e-2 ("AttnFuse", section 6.6 "Correctness").  The
+gradients here are stored in bf16, whose rounding alone is up to 2^-9 |g|
+and exceeds 2e-2 once |g| > 10 (dq and dk of rows with peaked softmax reach
+that), so the element bar is 2e-2 + 2^-8 |ref| (the absolute bar plus one
+bf16 ulp of the stored value).  The mean bar 2e-3 of the forward applies to
+the mean absolute error of each tensor.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from attention_attn_fwd_04_amd import binding
+from attention_attn_fwd_04_amd.inputs import bf16_bits, make_qkv
+from oracle import oracle as O
+
+pytestmark = pytest.mark.gpu
+
+ABS_TOL, REL_TOL, MEAN_TOL = 2e-2, 2.0 ** -8, 2e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+    yield
+    torch.cuda.synchronize()
+
+
+def _f64(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def _run(q, k, v, do, theta, causal, scale):
+    qd, kd, vd, dod = (t.cuda() for t in (q, k, v, do))
+    o, lse = binding.attn_fwd_lse(qd, kd, vd, rope_theta=theta, causal=causal, scale=scale)
+    dq, dk, dv = binding.attn_bwd(qd, kd, vd, o, lse, dod, rope_theta=theta, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return _f64(dq), _f64(dk), _f64(dv)
+
+
+def _check(got, ref, label):
+    for name, g, r in zip(("dq", "dk", "dv"), got, ref):
+        err = np.abs(g - r)
+        bar = ABS_TOL + REL_TOL * np.abs(r)
+        worst = np.unravel_index(np.argmax(err - bar), err.shape)
+        print("%s %s max_abs=%.3e mean_abs=%.3e max|ref|=%.3e worst=%s (err %.3e ref %.3e)"
+              % (label, name, err.max(), err.mean(), np.abs(r).max(), worst, err[worst], r[worst]), flush=True)
+        assert np.isfinite(g).all(), (label, name)
+        assert (err <= bar).all(), (label, name, worst)
+        if err.size >= 32:
+            assert err.mean() <= MEAN_TOL, (label, name, err.mean())
+
+
+CASES = [
+    # B, Hq, Hkv, S, D, theta, causal
+    (1, 2, 2, 256, 64, 1e4, True),       # the small prefill case
+    (2, 4, 2, 700, 128, 1e4, True),      # ragged tail, GQA 2:1
+    (1, 8, 2, 520, 128, 5e5, True),      # GQA 4:1
+    (1, 2, 2, 300, 128, 1e4, False),     # no causal mask, ragged
+    (1, 2, 2, 384, 128, 0.0, True),      # RoPE off
+    (1, 2, 1, 200, 64, 0.0, False),      # D = 64, no mask, no RoPE, GQA 2:1
+    (1, 3, 3, 33, 64, 1e4, True),        # one full tile plus one row
+    (1, 1, 1, 1, 128, 1e4, True),        # single token: dq = dk = 0, dv = do
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,S,D,theta,causal", CASES)
+def test_bwd_matches_oracle(B, Hq, Hkv, S, D, theta, causal):
+    label = "bwd %s" % ((B, Hq, Hkv, S, D, theta, causal),)
+    print(label, flush=True)
+    q, k, v = make_qkv(B, S, Hq, Hkv, D, seed=4000 + S + D)
+    do = make_qkv(B, S, Hq, Hkv, D, seed=5000 + S + D)[0]
+    scale = 1 / math.sqrt(D)
+    got = _run(q, k, v, do, theta, causal, scale)
+    ref = O.attn_bwd(bf16_bits(q), bf16_bits(k), bf16_bits(v), bf16_bits(do), theta, causal, scale)
+    _check(got, ref, label)
+
+
+def test_bwd_single_token_is_exact():
+    """One token: P = 1, so dv = do exactly and dq = dk = 0 (dS = 1 (dP - dP))."""
+    q, k, v = make_qkv(1, 1, 2, 2, 128, seed=91)
+    do = make_qkv(1, 1, 2, 2, 128, seed=92)[0]
+    dq, dk, dv = _run(q, k, v, do, 1e4, True, 0.1)
+    assert np.array_equal(dv, _f64(do))
+    assert np.abs(dq).max() <= 1e-3 and np.abs(dk).max() <= 1e-3
+
+
+def test_bwd_zero_queries_closed_form():
+    """q = 0 and RoPE off: causal row n is uniform over its n + 1 keys, so
+    dv[m] = sum_{n >= m} do[n] / (n + 1) (a suffix sum), and dk = scale
+    dS^T q = 0 exactly."""
+    B, H, S, D = 1, 2, 1000, 128
+    _, k, v = make_qkv(B, S, H, H, D, seed=93)
+    do = make_qkv(B, S, H, H, D, seed=94)[0]
+    q = torch.zeros(B, S, H, D, dtype=torch.bfloat16)
+    dq, dk, dv = _run(q, k, v, do, 0.0, True, 0.125)
+    w = _f64(do) / (np.arange(S, dtype=np.float64)[None, :, None, None] + 1)
+    ref = np.flip(np.cumsum(np.flip(w, axis=1), axis=1), axis=1)
+    err = np.abs(dv - ref)
+    print("zero-q dv max_abs=%.3e mean_abs=%.3e" % (err.max(), err.mean()), flush=True)
+    assert (err <= ABS_TOL + REL_TOL * np.abs(ref)).all()
+    assert err.mean() <= MEAN_TOL
+    assert not dk.any()
+    assert np.isfinite(dq).all()
+
+
+def test_bwd_rejects_window_and_small_workspace():
+    q, k, v = (t.cuda() for t in make_qkv(1, 64, 2, 2, 64, seed=95))
+    o, lse = binding.attn_fwd_lse(q, k, v, rope_theta=1e4)
+    w = O.window_table(1e4, 64, 1.0)
+    with pytest.raises(binding.AttnError) as e:
+        binding.attn_bwd(q, k, v, o, lse, q, window_table=w)
+    assert e.value.status == -2
+    small = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(binding.AttnError) as e:
+        binding.attn_bwd(q, k, v, o, lse, q, workspace=small)
+    assert e.value.status == -1

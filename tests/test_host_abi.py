@@ -187,3 +187,55 @@ def test_decode_rejects(kw, status):
 def test_decode_empty_is_ok_without_device():
     assert _dec_call(B=0, q=0, k=0, v=0, o=0, ws=0, nws=0) == binding.ATTN_OK
     assert _dec_call(L=0, q=0, k=0, v=0, o=0, ws=0, nws=0) == binding.ATTN_OK
+
+
+def test_bwd_workspace_bytes():
+    """Staged queries and keys (bf16) and Delta (fp32), 256-byte aligned
+    sections; 0 for empty or invalid sizes."""
+    ws = binding.attn_bwd_workspace_bytes
+    assert ws(0, 8, 2, 100, 128) == 0 and ws(1, 8, 2, 0, 128) == 0 and ws(1, 0, 2, 10, 128) == 0
+    B, Hq, Hkv, S, D = 2, 8, 2, 1000, 128
+    need = B * S * Hq * D * 2 + B * S * Hkv * D * 2 + B * Hq * S * 4
+    assert need <= ws(B, Hq, Hkv, S, D) <= need + 512
+
+
+def _bwd_call(**kw):
+    """attn_bwd with fake device addresses: only argument errors caught
+    before any device call are exercised here."""
+    a = dict(q=A, k=A * 64, v=A * 128, o=A * 192, do=A * 256, lse=A * 320, dq=A * 384, dk=A * 448, dv=A * 512,
+             ws=A * 576, nws=1 << 30, B=1, Hq=8, Hkv=2, S=100, D=128, theta=1e4, causal=1, scale=0.088, w=None)
+    a.update(kw)
+    return binding.lib().attn_bwd(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"],
+                                  a["ws"], a["nws"], a["B"], a["Hq"], a["Hkv"], a["S"], a["D"], a["theta"],
+                                  a["causal"], a["scale"], a["w"], None)
+
+
+_W = (ctypes.c_int32 * 64)(*range(64))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(w=_W), binding.ATTN_EUNSUPPORTED),           # no backward of the window
+    (dict(D=96), binding.ATTN_EUNSUPPORTED),
+    (dict(B=70000), binding.ATTN_EUNSUPPORTED),
+    (dict(Hq=5, Hkv=2), binding.ATTN_EINVAL),
+    (dict(causal=2), binding.ATTN_EINVAL),
+    (dict(scale=-1.0), binding.ATTN_EINVAL),
+    (dict(theta=0.5), binding.ATTN_EINVAL),
+    (dict(do=0), binding.ATTN_EINVAL),
+    (dict(lse=0), binding.ATTN_EINVAL),
+    (dict(ws=0), binding.ATTN_EINVAL),
+    (dict(dk=A * 448 + 8), binding.ATTN_EALIGN),
+    (dict(lse=A * 320 + 2), binding.ATTN_EALIGN),
+    (dict(nws=1024), binding.ATTN_EINVAL),               # workspace too small
+    (dict(dq=A), binding.ATTN_EINVAL),                   # dq aliases q
+    (dict(dv=A * 448), binding.ATTN_EINVAL),             # dv aliases dk
+    (dict(ws=A * 320), binding.ATTN_EINVAL),             # workspace overlaps lse
+])
+def test_bwd_rejects(kw, status):
+    assert _bwd_call(**kw) == status
+
+
+def test_bwd_empty_is_ok_without_device():
+    z = dict(q=0, k=0, v=0, o=0, do=0, lse=0, dq=0, dk=0, dv=0, ws=0, nws=0)
+    assert _bwd_call(B=0, **z) == binding.ATTN_OK
+    assert _bwd_call(S=0, **z) == binding.ATTN_OK
