@@ -31,6 +31,9 @@
 //    starts from -L log2 e, so P = exp2(accumulator).
 //  * With grouped heads the dK/dV kernel walks the group's query heads in
 //    turn, accumulating into the same registers.
+//  * Both gradient kernels fit 256 registers per lane, so two waves share
+//    each SIMD (two work-groups per CU): one wave's LDS waits and softmax
+//    arithmetic overlap the other's MFMAs.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -73,38 +76,52 @@ struct BGeo {
 // D0 + i of those 4 rows.  With the rows 16 ch + 4 g + (0..3) and the same
 // + 8, the 8 values of a lane follow the row order of the MFMA C layout,
 // which is the order of the P / dS operands built from an accumulator.
+// The per-lane byte offsets are recomputed from the lane index in every
+// tile (refresh() hides the index from loop-invariant code motion): 16
+// registers held across the loop would cost the kernels their second wave
+// per SIMD.
 template <int D>
 struct TileReader {
     using G = BGeo<D>;
-    int row_addr[G::KCH];
-    int tr_addr[G::DB][2];
-    __device__ __forceinline__ void init(int lane)
-    {
-        const int l32 = lane & 31, g = lane >> 5;
-#pragma unroll
-        for (int kc = 0; kc < G::KCH; ++kc) row_addr[kc] = G::off(l32, kc + G::PG * g);
-        const int tr_row = (lane & 15) >> 2;
-        const int tr_dim = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-#pragma unroll
-        for (int db = 0; db < G::DB; ++db)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) tr_addr[db][h] = G::dim_off(4 * g + tr_row + 8 * h, 32 * db + tr_dim);
-    }
+    int lane_;
+    __device__ __forceinline__ void init(int lane) { lane_ = lane; }
+    __device__ __forceinline__ void refresh() { asm volatile("" : "+v"(lane_)); }
     __device__ __forceinline__ bf16x8_t row(uint32_t base, int kc) const
     {
-        return *(const lds_bf16x8_t *)lds_ptr(base + (uint32_t)row_addr[kc]);
+        const int l32 = lane_ & 31, g = lane_ >> 5;
+        return *(const lds_bf16x8_t *)lds_ptr(base + (uint32_t)G::off(l32, kc + G::PG * g));
     }
     // rows 16 ch + ...: the chunk permutation repeats every 16 rows
     __device__ __forceinline__ bf16x8_t tr(uint32_t base, int ch, int db) const
     {
-        const lds_u8_t *p0 = lds_ptr(base + (uint32_t)tr_addr[db][0]) + 16 * ch * G::ROWB;
-        const lds_u8_t *p1 = lds_ptr(base + (uint32_t)tr_addr[db][1]) + 16 * ch * G::ROWB;
+        const int g = lane_ >> 5;
+        const int tr_row = (lane_ & 15) >> 2;
+        const int tr_dim = 16 * ((lane_ >> 4) & 1) + 4 * (lane_ & 3);
+        const lds_u8_t *p0 = lds_ptr(base + (uint32_t)G::dim_off(4 * g + tr_row, 32 * db + tr_dim)) + 16 * ch * G::ROWB;
+        const lds_u8_t *p1 =
+            lds_ptr(base + (uint32_t)G::dim_off(4 * g + tr_row + 8, 32 * db + tr_dim)) + 16 * ch * G::ROWB;
         const i16x4_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)p0);
         const i16x4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)p1);
         const uint2 u0 = __builtin_bit_cast(uint2, t0), u1 = __builtin_bit_cast(uint2, t1);
         return __builtin_bit_cast(bf16x8_t, make_uint4(u0.x, u0.y, u1.x, u1.y));
     }
 };
+
+// Instruction order of one block of MFMAs fed from LDS: the first group of
+// reads, then alternately two MFMAs and the reads of the next two (the
+// scheduler otherwise issues each read right before its MFMA and waits on
+// it).  n_mfma MFMAs, reads_per_mfma LDS reads each.
+template <int n_mfma, int reads_per_mfma>
+__device__ __forceinline__ void interleave_reads_mfma()
+{
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * reads_per_mfma, 0);   // DS reads
+#pragma unroll
+    for (int j = 0; j < n_mfma / 2 - 1; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * reads_per_mfma, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+}
 
 // Direct loads of one 32-row tile (rows row0 .. row0 + 31 of a tensor whose
 // rows are row_b bytes apart, D bf16 values each) into LDS at lds_dst in the
@@ -230,7 +247,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdArgs a, long lon
 
 // ---- dQ: per 128-query tile and head, keys streamed -----------------------
 template <int D, bool CAUSAL, bool ROPE>
-__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(const BwdArgs a)
+__global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(const BwdArgs a)
 {
     using G = BGeo<D>;
     __shared__ __attribute__((aligned(16))) uint8_t smem[4 * G::TILE_B];   // K' and V, two slots each
@@ -242,16 +259,19 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(const BwdArgs a)
     const int n0 = qt * kBwdBM, nw0 = n0 + wave * 32, n = nw0 + l32;
 
     // Resident B operands: the staged query (c R(n) q) and dO of the lane's
-    // query, zero past S.
-    bf16x8_t qreg[G::KCH], doreg[G::KCH];
+    // query (buffer loads: zero past S).
+    const uint32_t q_rowb = (uint32_t)a.Hq * D * 2;
     const size_t qoff = (((size_t)b * S + n) * a.Hq + hq) * D;
+    bf16x8_t qreg[G::KCH], doreg[G::KCH];
+    {
+        const __amdgpu_buffer_rsrc_t q_rs = make_rsrc(a.qs + ((size_t)b * S * a.Hq + hq) * D, (uint32_t)S * q_rowb);
+        const __amdgpu_buffer_rsrc_t d_rs = make_rsrc(a.dout + ((size_t)b * S * a.Hq + hq) * D, (uint32_t)S * q_rowb);
 #pragma unroll
-    for (int kc = 0; kc < G::KCH; ++kc) {
-        const int d = 8 * kc + (D / 2) * g;
-        const uint4 zq = n < S ? *reinterpret_cast<const uint4 *>(a.qs + qoff + d) : make_uint4(0, 0, 0, 0);
-        const uint4 zd = n < S ? *reinterpret_cast<const uint4 *>(a.dout + qoff + d) : make_uint4(0, 0, 0, 0);
-        qreg[kc] = __builtin_bit_cast(bf16x8_t, zq);
-        doreg[kc] = __builtin_bit_cast(bf16x8_t, zd);
+        for (int kc = 0; kc < G::KCH; ++kc) {
+            const uint32_t off = (uint32_t)n * q_rowb + 2u * (uint32_t)(8 * kc + (D / 2) * g);
+            qreg[kc] = __builtin_bit_cast(bf16x8_t, bload16(q_rs, off));
+            doreg[kc] = __builtin_bit_cast(bf16x8_t, bload16(d_rs, off));
+        }
     }
     const size_t rowid = ((size_t)b * a.Hq + hq) * S + n;
     const float L2 = n < S ? a.lse[rowid] * kLog2e : 0.f;
@@ -288,6 +308,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(const BwdArgs a)
         const int m0 = t * kBwdBN;
         if (m0 >= wave_end) continue;   // wave-uniform: all keys after this wave's queries
         const uint32_t kb = kslot(t), vb = vslot(t);
+        rd.refresh();
         // S^T (exp2 domain, minus L log2 e) and dP^T = V dO^T: rows keys, columns queries
         f32x16_t s, dp;
 #pragma unroll
@@ -295,11 +316,14 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(const BwdArgs a)
             s[i] = -L2;
             dp[i] = 0.f;
         }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int kc = 0; kc < G::KCH; ++kc) {
             s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd.row(kb, kc), qreg[kc], s, 0, 0, 0);
             dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd.row(vb, kc), doreg[kc], dp, 0, 0, 0);
         }
+        interleave_reads_mfma<2 * G::KCH, 1>();
+        __builtin_amdgcn_sched_barrier(0);
         // dS^T = P^T o (dP^T - Delta) with masked P set to zero
         bf16x8_t dsop[2];
 #pragma unroll
@@ -321,11 +345,14 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(const BwdArgs a)
             dsop[ch] = __builtin_bit_cast(bf16x8_t, make_uint4(w4[0], w4[1], w4[2], w4[3]));
         }
         // dQ'^T += K'^T dS^T
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ch = 0; ch < 2; ++ch)
 #pragma unroll
             for (int db = 0; db < G::DB; ++db)
                 acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd.tr(kb, ch, db), dsop[ch], acc[db], 0, 0, 0);
+        interleave_reads_mfma<2 * G::DB, 2>();
+        __builtin_amdgcn_sched_barrier(0);
     }
     if (n >= S) return;
     if constexpr (ROPE) unrotate_acc<D>(acc, a.rope_cs, n, g);
@@ -334,7 +361,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(const BwdArgs a)
 
 // ---- dK, dV: per 128-key tile and KV head, queries streamed ----------------
 template <int D, bool CAUSAL, bool ROPE>
-__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(const BwdArgs a)
+__global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkdv_kernel(const BwdArgs a)
 {
     using G = BGeo<D>;
     __shared__ __attribute__((aligned(16))) uint8_t smem[4 * G::TILE_B];   // Q and dO, two slots each
@@ -346,16 +373,20 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(const BwdArgs 
     const int S = a.S, grp = a.Hq / a.Hkv;
     const int m0 = kt * kBwdBM, mw0 = m0 + wave * 32, m = mw0 + l32;
 
-    // Resident B operands: K' and V of the lane's key, zero past S.
-    bf16x8_t kreg[G::KCH], vreg[G::KCH];
+    // Resident B operands: K' and V of the lane's key (buffer loads: zero
+    // past S).
+    const uint32_t kv_rowb = (uint32_t)a.Hkv * D * 2;
     const size_t koff = (((size_t)b * S + m) * a.Hkv + hk) * D;
+    bf16x8_t kreg[G::KCH], vreg[G::KCH];
+    {
+        const __amdgpu_buffer_rsrc_t k_rs = make_rsrc(a.kop + ((size_t)b * S * a.Hkv + hk) * D, (uint32_t)S * kv_rowb);
+        const __amdgpu_buffer_rsrc_t v_rs = make_rsrc(a.v + ((size_t)b * S * a.Hkv + hk) * D, (uint32_t)S * kv_rowb);
 #pragma unroll
-    for (int kc = 0; kc < G::KCH; ++kc) {
-        const int d = 8 * kc + (D / 2) * g;
-        const uint4 zk = m < S ? *reinterpret_cast<const uint4 *>(a.kop + koff + d) : make_uint4(0, 0, 0, 0);
-        const uint4 zv = m < S ? *reinterpret_cast<const uint4 *>(a.v + koff + d) : make_uint4(0, 0, 0, 0);
-        kreg[kc] = __builtin_bit_cast(bf16x8_t, zk);
-        vreg[kc] = __builtin_bit_cast(bf16x8_t, zv);
+        for (int kc = 0; kc < G::KCH; ++kc) {
+            const uint32_t off = (uint32_t)m * kv_rowb + 2u * (uint32_t)(8 * kc + (D / 2) * g);
+            kreg[kc] = __builtin_bit_cast(bf16x8_t, bload16(k_rs, off));
+            vreg[kc] = __builtin_bit_cast(bf16x8_t, bload16(v_rs, off));
+        }
     }
 
     const uint32_t q_rowb = (uint32_t)a.Hq * D * 2;
@@ -419,6 +450,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(const BwdArgs 
         const int n0 = (t0 + u % nt) * kBwdBN;
         if (CAUSAL && n0 + kBwdBN - 1 < mw0) continue;   // wave-uniform: all queries before this wave's keys
         const uint32_t qb = qslot(u), dbs = dslot(u);
+        rd.refresh();
         const float *lrow = rowv[u & 1][0], *drow = rowv[u & 1][1];
         // S = Q K'^T (exp2 domain, minus L log2 e) and dP = dO V^T: rows queries, columns keys
         f32x16_t s, dp;
@@ -432,11 +464,14 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(const BwdArgs 
         }
 #pragma unroll
         for (int i = 0; i < 16; ++i) dp[i] = 0.f;
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int kc = 0; kc < G::KCH; ++kc) {
             s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd.row(qb, kc), kreg[kc], s, 0, 0, 0);
             dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd.row(dbs, kc), vreg[kc], dp, 0, 0, 0);
         }
+        interleave_reads_mfma<2 * G::KCH, 1>();
+        __builtin_amdgcn_sched_barrier(0);
         // P and dS = P o (dP - Delta), masked entries zero
         bf16x8_t pop[2], dsop[2];
 #pragma unroll
@@ -464,6 +499,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(const BwdArgs 
             dsop[ch] = __builtin_bit_cast(bf16x8_t, make_uint4(wd[0], wd[1], wd[2], wd[3]));
         }
         // dV^T += dO^T P, dK'^T += Q^T dS
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ch = 0; ch < 2; ++ch)
 #pragma unroll
@@ -471,6 +507,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(const BwdArgs 
                 dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd.tr(dbs, ch, db), pop[ch], dv[db], 0, 0, 0);
                 dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd.tr(qb, ch, db), dsop[ch], dk[db], 0, 0, 0);
             }
+        interleave_reads_mfma<4 * G::DB, 2>();
+        __builtin_amdgcn_sched_barrier(0);
     }
     if (m >= S) return;
     store_acc<D>(a.dv + koff, dv, 1.0f, g);

@@ -403,6 +403,156 @@ int oracle_attn_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
 }
 
 /*
+ * The per-row terms of the backward above for one query row (b, n, hq),
+ * given the rotated keys kr of its KV head: the rotated query qr, the
+ * upstream row dor, the probabilities p[m] and dS[m] = p[m] (dP[m] - Delta)
+ * over the visible keys m < m_end, which is returned.
+ */
+static int bwd_row_terms(const uint16_t *q, const uint16_t *v,
+                         const uint16_t *dout, int S, int Hq, int Hkv, int D,
+                         double theta, int causal, double scale, int b, int n,
+                         int hq, int hk, const double *kr, double *qr,
+                         double *dor, double *p, double *ds)
+{
+    double qraw[1024];
+    const uint16_t *qs = row_ptr(q, S, Hq, D, b, n, hq);
+    const uint16_t *dsrc = row_ptr(dout, S, Hq, D, b, n, hq);
+    for (int d = 0; d < D; ++d) {
+        qraw[d] = widen_bf16(qs[d]);
+        dor[d] = widen_bf16(dsrc[d]);
+    }
+    rotate_row(qraw, D, theta, (double)n, qr);
+    int m_end = causal ? n + 1 : S;
+    double mu = -INFINITY;
+    for (int m = 0; m < m_end; ++m) {
+        p[m] = score(qr, kr + (size_t)m * D, D, scale, NULL, 0);
+        if (p[m] > mu)
+            mu = p[m];
+    }
+    double z = 0.0;
+    for (int m = 0; m < m_end; ++m) {
+        p[m] = exp(p[m] - mu);
+        z += p[m];
+    }
+    double delta = 0.0;
+    for (int m = 0; m < m_end; ++m) {
+        p[m] /= z;
+        const uint16_t *vs = row_ptr(v, S, Hkv, D, b, m, hk);
+        double acc = 0.0;
+        for (int d = 0; d < D; ++d)
+            acc += dor[d] * widen_bf16(vs[d]);
+        ds[m] = acc;
+        delta += p[m] * acc;
+    }
+    for (int m = 0; m < m_end; ++m)
+        ds[m] = p[m] * (ds[m] - delta);
+    return m_end;
+}
+
+/*
+ * Entries of the backward above at full size, one at a time: dq of the
+ * query rows qrows (n_q triples b, n, hq) and dk, dv of the key rows kcols
+ * (n_k triples b, m, hk).  A query row costs one score row; a key row costs
+ * one score row per query that sees it (S - m of them per query head under
+ * the causal mask).  dq_out: n_q x D, dk_out, dv_out: n_k x D (fp64).
+ */
+int oracle_attn_bwd_sampled(const uint16_t *q, const uint16_t *k,
+                            const uint16_t *v, const uint16_t *dout, int B,
+                            int S, int Hq, int Hkv, int D, double rope_theta,
+                            int causal, double scale, const int32_t *qrows,
+                            int n_q, double *dq_out, const int32_t *kcols,
+                            int n_k, double *dk_out, double *dv_out)
+{
+    if (B < 0 || S < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || D > 1024 ||
+        (D % 2) != 0 || (Hq % Hkv) != 0 || n_q < 0 || n_k < 0)
+        return -1;
+    int group = Hq / Hkv;
+    for (int i = 0; i < n_q + n_k; ++i) {
+        const int32_t *t = i < n_q ? qrows + 3 * i : kcols + 3 * (i - n_q);
+        if (t[0] < 0 || t[0] >= B || t[1] < 0 || t[1] >= S || t[2] < 0 ||
+            t[2] >= (i < n_q ? Hq : Hkv))
+            return -1;
+    }
+    for (int i = 0; i < n_q; ++i) {
+        int b = qrows[3 * i], n = qrows[3 * i + 1], hq = qrows[3 * i + 2];
+        int hk = hq / group;
+        double *kr = rotated_keys(k, S, Hkv, D, b, hk, rope_theta, 0);
+        double *p = (double *)malloc(sizeof(double) * (size_t)S);
+        double *ds = (double *)malloc(sizeof(double) * (size_t)S);
+        if (!kr || !p || !ds) {
+            free(kr);
+            free(p);
+            free(ds);
+            return -1;
+        }
+        double qr[1024], dor[1024], dqr[1024];
+        int m_end = bwd_row_terms(q, v, dout, S, Hq, Hkv, D, rope_theta, causal,
+                                  scale, b, n, hq, hk, kr, qr, dor, p, ds);
+        for (int d = 0; d < D; ++d)
+            dqr[d] = 0.0;
+        for (int m = 0; m < m_end; ++m)
+            for (int d = 0; d < D; ++d)
+                dqr[d] += scale * ds[m] * kr[(size_t)m * D + d];
+        unrotate_row(dqr, D, rope_theta, (double)n);
+        memcpy(dq_out + (size_t)i * D, dqr, sizeof(double) * (size_t)D);
+        free(kr);
+        free(p);
+        free(ds);
+    }
+    for (int j = 0; j < n_k; ++j) {
+        int b = kcols[3 * j], m = kcols[3 * j + 1], hk = kcols[3 * j + 2];
+        double *kr = rotated_keys(k, S, Hkv, D, b, hk, rope_theta, 0);
+        if (!kr)
+            return -1;
+        double dkr[1024], dvr[1024];
+        for (int d = 0; d < D; ++d)
+            dkr[d] = dvr[d] = 0.0;
+        int fail = 0;
+        for (int g = 0; g < group; ++g) {
+            int hq = hk * group + g;
+#pragma omp parallel
+            {
+                double dk_t[1024], dv_t[1024], qr[1024], dor[1024];
+                double *p = (double *)malloc(sizeof(double) * (size_t)S);
+                double *ds = (double *)malloc(sizeof(double) * (size_t)S);
+                for (int d = 0; d < D; ++d)
+                    dk_t[d] = dv_t[d] = 0.0;
+                if (p && ds) {
+#pragma omp for schedule(dynamic, 1)
+                    for (int n = causal ? m : 0; n < S; ++n) {
+                        bwd_row_terms(q, v, dout, S, Hq, Hkv, D, rope_theta,
+                                      causal, scale, b, n, hq, hk, kr, qr, dor,
+                                      p, ds);
+                        for (int d = 0; d < D; ++d) {
+                            dv_t[d] += p[m] * dor[d];
+                            dk_t[d] += scale * ds[m] * qr[d];
+                        }
+                    }
+                }
+#pragma omp critical
+                {
+                    if (!p || !ds)
+                        fail = 1;
+                    for (int d = 0; d < D; ++d) {
+                        dkr[d] += dk_t[d];
+                        dvr[d] += dv_t[d];
+                    }
+                }
+                free(p);
+                free(ds);
+            }
+        }
+        free(kr);
+        if (fail)
+            return -1;
+        unrotate_row(dkr, D, rope_theta, (double)m);
+        memcpy(dk_out + (size_t)j * D, dkr, sizeof(double) * (size_t)D);
+        memcpy(dv_out + (size_t)j * D, dvr, sizeof(double) * (size_t)D);
+    }
+    return 0;
+}
+
+/*
  * The scaled score row s(n, m) for m = 0..S-1 of one query (b, n, hq), with
  * masked keys (m > n under the causal mask) set to -inf.  Used by the
  * invariance and window tests.

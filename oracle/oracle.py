@@ -57,6 +57,11 @@ def _load():
                                     ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_int, ctypes.c_double,
                                     f64p, f64p, f64p]
     lib.oracle_attn_bwd.restype = ctypes.c_int
+    lib.oracle_attn_bwd_sampled.argtypes = [u16p, u16p, u16p, u16p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                            ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_int,
+                                            ctypes.c_double, i32p, ctypes.c_int, f64p, i32p, ctypes.c_int, f64p,
+                                            f64p]
+    lib.oracle_attn_bwd_sampled.restype = ctypes.c_int
     lib.oracle_scores_row.argtypes = [u16p, u16p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                       ctypes.c_int, ctypes.c_int, ctypes.c_double,
                                       ctypes.c_int, ctypes.c_double, i32p,
@@ -153,6 +158,30 @@ def attn_bwd(q, k, v, do, rope_theta, causal, scale):
                              int(bool(causal)), float(scale), f(dq), f(dk), f(dv))
     if rc != 0:
         raise ValueError("oracle_attn_bwd rejected its arguments")
+    return dq, dk, dv
+
+
+def attn_bwd_sampled(q, k, v, do, rope_theta, causal, scale, qrows, kcols):
+    """Single entries of attn_bwd at any size: dq of the query rows qrows
+    ((b, n, hq) triples) and dk, dv of the key rows kcols ((b, m, hk)).
+    Returns dq [len(qrows), D], dk, dv [len(kcols), D] (fp64)."""
+    lib = _load()
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    assert k.shape == (B, S, Hkv, D) and v.shape == k.shape and do.shape == q.shape
+    q, k, v, do = (np.ascontiguousarray(t) for t in (q, k, v, do))
+    qr = np.ascontiguousarray(np.asarray(qrows, dtype=np.int32).reshape(-1, 3))
+    kc = np.ascontiguousarray(np.asarray(kcols, dtype=np.int32).reshape(-1, 3))
+    dq = np.zeros((len(qr), D), dtype=np.float64)
+    dk = np.zeros((len(kc), D), dtype=np.float64)
+    dv = np.zeros((len(kc), D), dtype=np.float64)
+    f = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+    i = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    rc = lib.oracle_attn_bwd_sampled(_u16(q), _u16(k), _u16(v), _u16(do), B, S, Hq, Hkv, D, float(rope_theta),
+                                     int(bool(causal)), float(scale), i(qr), len(qr), f(dq), i(kc), len(kc),
+                                     f(dk), f(dv))
+    if rc != 0:
+        raise ValueError("oracle_attn_bwd_sampled rejected its arguments")
     return dq, dk, dv
 
 

@@ -18,7 +18,7 @@ import pytest
 import torch
 
 from attention_attn_fwd_04_amd import binding
-from attention_attn_fwd_04_amd.inputs import bf16_bits, make_qkv
+from attention_attn_fwd_04_amd.inputs import CONFIGS, CONFIG_SEEDS, bf16_bits, make_qkv
 from oracle import oracle as O
 
 pytestmark = pytest.mark.gpu
@@ -124,3 +124,31 @@ def test_bwd_rejects_window_and_small_workspace():
     with pytest.raises(binding.AttnError) as e:
         binding.attn_bwd(q, k, v, o, lse, q, workspace=small)
     assert e.value.status == -1
+
+
+@pytest.mark.parametrize("name", ["prefill_s8192", "gqa_s16384"])
+def test_bwd_full_size_sampled(name):
+    """The full workloads in the launch configuration the benchmark times
+    (attn_fwd_lse then attn_bwd, causal, RoPE): sampled dq rows anywhere in
+    the sequence and dk, dv rows of late keys, each against the oracle's
+    one-entry computation."""
+    c = CONFIGS[name]
+    B, Hq, Hkv, S, D, theta = c["B"], c["Hq"], c["Hkv"], c["S"], c["D"], c["theta"]
+    print("bwd full size %s" % name, flush=True)
+    q, k, v = make_qkv(B, S, Hq, Hkv, D, seed=CONFIG_SEEDS[name])
+    do = make_qkv(B, S, Hq, Hkv, D, seed=CONFIG_SEEDS[name] + 1000)[0]
+    scale = 1 / math.sqrt(D)
+    qd, kd, vd, dod = (t.cuda() for t in (q, k, v, do))
+    o, lse = binding.attn_fwd_lse(qd, kd, vd, rope_theta=theta, causal=True, scale=scale)
+    dq, dk, dv = binding.attn_bwd(qd, kd, vd, o, lse, dod, rope_theta=theta, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    qrows = [(0, 0, 0), (0, S - 1, 0), (B - 1, S // 2 + 17, Hq - 1), (B - 1, 129, 5), (0, 4095, 7)]
+    kcols = [(0, S - 1, 0), (B - 1, S - 33, Hkv - 1), (0, S - 70, 1)]
+    rq, rk, rv = O.attn_bwd_sampled(bf16_bits(q), bf16_bits(k), bf16_bits(v), bf16_bits(do), theta, True, scale,
+                                    qrows, kcols)
+    gq = np.array([_f64(dq[b, n, h]) for b, n, h in qrows])
+    gk = np.array([_f64(dk[b, m, h]) for b, m, h in kcols])
+    gv = np.array([_f64(dv[b, m, h]) for b, m, h in kcols])
+    _check((gq, gk, gv), (rq, rk, rv), "bwd %s sampled" % name)
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t.float()).all()

@@ -546,3 +546,32 @@ def test_bwd_closed_forms():
     _, dk2, _ = O.attn_bwd(q, k, v, do, 0.0, True, 0.125)
     # sum over keys of dk'[m] = scale * sum_n q'[n] * sum_m dS[n, m] = 0
     np.testing.assert_allclose(dk2[0, :, 0].sum(axis=0), 0.0, atol=1e-12)
+
+
+@pytest.mark.parametrize("B,S,Hq,Hkv,D,theta,causal", [
+    (2, 37, 4, 2, 64, 1e4, True),
+    (1, 29, 2, 1, 128, 5e5, False),
+    (1, 24, 2, 2, 64, 0.0, True),
+])
+def test_bwd_sampled_matches_torch_autograd_fp64(B, S, Hq, Hkv, D, theta, causal):
+    """The one-entry-at-a-time backward (used at full sizes) against torch's
+    fp64 autograd of SDPA with the rotation, on every query row and key row
+    of small cases, including the first key (seen by every query)."""
+    q, k, v = _qkv_np(B, S, Hq, Hkv, D, seed=700 + S)
+    do = _qkv_np(B, S, Hq, Hkv, D, seed=800 + S)[0]
+    scale = 1 / math.sqrt(D)
+    qrows = [(b, n, h) for b in range(B) for n in range(S) for h in range(Hq)]
+    kcols = [(b, m, h) for b in range(B) for m in range(S) for h in range(Hkv)]
+    dq, dk, dv = O.attn_bwd_sampled(q, k, v, do, theta, causal, scale, qrows, kcols)
+    rq, rk, rv = _torch_grads(q, k, v, do, theta, causal, scale)
+    np.testing.assert_allclose(dq, np.array([rq[b, n, h] for b, n, h in qrows]), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dk, np.array([rk[b, m, h] for b, m, h in kcols]), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dv, np.array([rv[b, m, h] for b, m, h in kcols]), rtol=0, atol=1e-11)
+
+
+def test_bwd_sampled_rejects_out_of_range_rows():
+    q, k, v = _qkv_np(1, 8, 2, 1, 64, seed=9)
+    with pytest.raises(ValueError):
+        O.attn_bwd_sampled(q, k, v, q, 1e4, True, 0.1, [(0, 8, 0)], [])
+    with pytest.raises(ValueError):
+        O.attn_bwd_sampled(q, k, v, q, 1e4, True, 0.1, [], [(0, 0, 1)])
