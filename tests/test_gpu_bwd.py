@@ -8,8 +8,10 @@ fp16 bar, |err| < 2e-2 ("AttnFuse", section 6.6 "Correctness").  The
 gradients here are stored in bf16, whose rounding alone is up to 2^-9 |g|
 and exceeds 2e-2 once |g| > 10 (dq and dk of rows with peaked softmax reach
 that), so the element bar is 2e-2 + 2^-8 |ref| (the absolute bar plus one
-bf16 ulp of the stored value).  The mean bar 2e-3 of the forward applies to
-the mean absolute error of each tensor.
+bf16 ulp of the stored value).  The mean bar is the forward's 2e-3 plus the
+same relative term over the tensor, 2e-3 + 2^-8 mean|ref|: the dominant
+error, Delta = rowsum(dO o O) taken from the bf16 forward output and dS
+rounded to bf16, grows with |dP| = |<dO, V>|, i.e. with the gradients.
 """
 import math
 
@@ -57,7 +59,7 @@ def _check(got, ref, label):
         assert np.isfinite(g).all(), (label, name)
         assert (err <= bar).all(), (label, name, worst)
         if err.size >= 32:
-            assert err.mean() <= MEAN_TOL, (label, name, err.mean())
+            assert err.mean() <= MEAN_TOL + REL_TOL * np.abs(r).mean(), (label, name, err.mean())
 
 
 CASES = [
@@ -108,7 +110,7 @@ def test_bwd_zero_queries_closed_form():
     err = np.abs(dv - ref)
     print("zero-q dv max_abs=%.3e mean_abs=%.3e" % (err.max(), err.mean()), flush=True)
     assert (err <= ABS_TOL + REL_TOL * np.abs(ref)).all()
-    assert err.mean() <= MEAN_TOL
+    assert err.mean() <= MEAN_TOL + REL_TOL * np.abs(ref).mean()
     assert not dk.any()
     assert np.isfinite(dq).all()
 

@@ -1,0 +1,156 @@
+"""Property fuzzing of the GPU path against the fp64 oracle, through the C ABI.
+
+Hypothesis draws the configuration (batch, head grouping, sequence length
+including ragged tails and single tokens, head dimension, RoPE theta on or
+off, causal or full, the per-pair window, the input distribution and seed)
+and each property compares the whole output with the oracle at the bars of
+the fixed-case tests: max |err| <= 2e-2 and mean |err| <= 2e-3 for outputs
+and LSE; 2e-2 + 2^-8 |ref| per gradient element and 2e-3 + 2^-8 mean|ref|
+for a gradient's mean error.  The runs are derandomized,
+so every execution checks the same examples (AttnFuse, section 6.6
+"Correctness", fuzzes forward and backward configurations the same way).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+from hypothesis import HealthCheck, given, settings
+from hypothesis import strategies as st
+
+from attention_attn_fwd_04_amd import binding
+from attention_attn_fwd_04_amd.inputs import bf16_bits, make_qkv
+from oracle import oracle as O
+
+pytestmark = pytest.mark.gpu
+
+MAX_TOL, MEAN_TOL = 2e-2, 2e-3
+FUZZ = settings(max_examples=40, deadline=None, derandomize=True, database=None,
+                suppress_health_check=[HealthCheck.too_slow, HealthCheck.data_too_large])
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+    yield
+    torch.cuda.synchronize()
+
+
+@st.composite
+def prefill_cases(draw, window_ok=True, max_s=300):
+    B = draw(st.integers(1, 2))
+    Hkv = draw(st.sampled_from([1, 2, 4]))
+    G = draw(st.sampled_from([1, 2, 4]))
+    S = draw(st.one_of(st.integers(1, 40), st.integers(1, max_s)))
+    D = draw(st.sampled_from([64, 128]))
+    theta = draw(st.sampled_from([0.0, 1e4, 5e5]))
+    causal = draw(st.booleans())
+    wk = None
+    if window_ok and causal and theta > 0:
+        wk = draw(st.sampled_from([None, None, 0.25, 1.0, 4.0]))
+    scale = draw(st.sampled_from([1.0, 0.5])) / math.sqrt(D)
+    dist = draw(st.sampled_from(["normal", "uniform"]))
+    seed = draw(st.integers(0, 2 ** 20))
+    return dict(B=B, Hq=Hkv * G, Hkv=Hkv, S=S, D=D, theta=theta, causal=causal, wk=wk, scale=scale,
+                dist=dist, seed=seed)
+
+
+def _bar(name, got, ref):
+    err = np.abs(got.astype(np.float64) - ref)
+    assert np.isfinite(got).all(), name
+    assert err.max() <= MAX_TOL, (name, float(err.max()))
+    if err.size >= 32:
+        assert err.mean() <= MEAN_TOL, (name, float(err.mean()))
+
+
+@FUZZ
+@given(c=prefill_cases())
+def test_fuzz_forward_and_lse(c):
+    print("fuzz fwd %s" % c, flush=True)
+    q, k, v = make_qkv(c["B"], c["S"], c["Hq"], c["Hkv"], c["D"], seed=c["seed"], dist=c["dist"])
+    window = O.window_table(c["theta"], c["D"], c["wk"]) if c["wk"] else None
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    o, lse = binding.attn_fwd_lse(qd, kd, vd, rope_theta=c["theta"], causal=c["causal"], scale=c["scale"],
+                                  window_table=window)
+    o2 = binding.attn_fwd(qd, kd, vd, rope_theta=c["theta"], causal=c["causal"], scale=c["scale"],
+                          window_table=window)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16))
+    rows = O.all_rows(c["B"], c["S"], c["Hq"])
+    ref, ref_lse = O.attn_rows(bf16_bits(q), bf16_bits(k), bf16_bits(v), rows, c["theta"], c["causal"],
+                               c["scale"], window, want_lse=True)
+    got = o.float().cpu().numpy()
+    gl = lse.cpu().numpy()
+    _bar("o", np.array([got[b, n, h] for b, n, h in rows]), ref)
+    _bar("lse", np.array([gl[b, h, n] for b, n, h in rows]), ref_lse)
+
+
+@FUZZ
+@given(c=prefill_cases(window_ok=False, max_s=200))
+def test_fuzz_backward(c):
+    print("fuzz bwd %s" % c, flush=True)
+    q, k, v = make_qkv(c["B"], c["S"], c["Hq"], c["Hkv"], c["D"], seed=c["seed"], dist=c["dist"])
+    do = make_qkv(c["B"], c["S"], c["Hq"], c["Hkv"], c["D"], seed=c["seed"] + 1)[0]
+    qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    o, lse = binding.attn_fwd_lse(qd, kd, vd, rope_theta=c["theta"], causal=c["causal"], scale=c["scale"])
+    dq, dk, dv = binding.attn_bwd(qd, kd, vd, o, lse, dod, rope_theta=c["theta"], causal=c["causal"],
+                                  scale=c["scale"])
+    torch.cuda.synchronize()
+    ref = O.attn_bwd(bf16_bits(q), bf16_bits(k), bf16_bits(v), bf16_bits(do), c["theta"], c["causal"], c["scale"])
+    for name, g, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+        g = g.float().cpu().numpy().astype(np.float64)
+        err = np.abs(g - r)
+        assert np.isfinite(g).all(), name
+        assert (err <= MAX_TOL + 2.0 ** -8 * np.abs(r)).all(), (name, float(err.max()))
+        if err.size >= 32:
+            assert err.mean() <= MEAN_TOL + 2.0 ** -8 * np.abs(r).mean(), (name, float(err.mean()))
+
+
+@st.composite
+def decode_cases(draw):
+    B = draw(st.integers(1, 3))
+    Hkv = draw(st.sampled_from([1, 2, 8]))
+    G = draw(st.sampled_from([1, 2, 4, 8]))
+    L = draw(st.one_of(st.integers(1, 64), st.integers(1, 3000)))
+    D = draw(st.sampled_from([64, 128]))
+    theta = draw(st.sampled_from([0.0, 1e4, 5e5]))
+    wk = draw(st.sampled_from([None, None, 0.5, 2.0])) if theta > 0 else None
+    splits = draw(st.sampled_from([0, 0, 1, 3, 16, 1000]))
+    seed = draw(st.integers(0, 2 ** 20))
+    return dict(B=B, Hq=Hkv * G, Hkv=Hkv, L=L, D=D, theta=theta, wk=wk, splits=splits, seed=seed)
+
+
+@FUZZ
+@given(c=decode_cases())
+def test_fuzz_decode(c):
+    print("fuzz decode %s" % c, flush=True)
+    q, k, v = make_qkv(c["B"], c["L"], c["Hq"], c["Hkv"], c["D"], seed=c["seed"])
+    q = q[:, -1].contiguous()
+    scale = 1 / math.sqrt(c["D"])
+    window = O.window_table(c["theta"], c["D"], c["wk"]) if c["wk"] else None
+    o, lse = binding.attn_decode(q.cuda(), k.cuda(), v.cuda(), rope_theta=c["theta"], scale=scale,
+                                 window_table=window, num_splits=c["splits"], want_lse=True)
+    torch.cuda.synchronize()
+    ref, ref_lse = O.decode(bf16_bits(q), bf16_bits(k), bf16_bits(v), c["theta"], scale, window, want_lse=True)
+    _bar("o", o.float().cpu().numpy(), ref)
+    _bar("lse", lse.cpu().numpy(), ref_lse)
+
+
+@FUZZ
+@given(c=prefill_cases(window_ok=False))
+def test_fuzz_separate_rope_pass(c):
+    """The separate path (RoPE pass, then attention with RoPE off) against the
+    oracle with RoPE on; the pass's keys equal the oracle's rotation rounded."""
+    if c["theta"] == 0.0:
+        c["theta"] = 1e4
+    print("fuzz separate %s" % c, flush=True)
+    q, k, v = make_qkv(c["B"], c["S"], c["Hq"], c["Hkv"], c["D"], seed=c["seed"], dist=c["dist"])
+    qr, kr = binding.attn_rope_apply(q.cuda(), k.cuda(), rope_theta=c["theta"])
+    o = binding.attn_fwd(qr, kr, v.cuda(), rope_theta=0.0, causal=c["causal"], scale=c["scale"])
+    torch.cuda.synchronize()
+    rows = O.all_rows(c["B"], c["S"], c["Hq"])
+    ref = O.attn_rows(bf16_bits(q), bf16_bits(k), bf16_bits(v), rows, c["theta"], c["causal"], c["scale"])
+    got = o.float().cpu().numpy()
+    _bar("o", np.array([got[b, n, h] for b, n, h in rows]), ref)
