@@ -61,8 +61,17 @@ struct BGeo {
     static constexpr int NI_W = NI / kBwdWaves;
     static constexpr int RPI = 1024 / ROWB;
     static_assert(NI % kBwdWaves == 0, "direct loads split over the waves");
-    // 16-byte chunks XOR-permuted per row (the prefill kernel's K layout).
-    static __device__ __forceinline__ int kx(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+    // 16-byte chunks XOR-permuted per row.  The streamed tiles are read both
+    // as rows (ds_read_b128: 16 lanes, 16 consecutive rows, one logical
+    // chunk) and transposed (ds_read_b64_tr_b16: 32 lanes, 4 consecutive rows
+    // x 4 consecutive chunks), so the permutation must spread both over the
+    // 16 four-bank groups of a 256-byte bank cycle: it is injective over 16
+    // rows and its top two bits differ among any 4 aligned rows (for D = 64,
+    // two rows share a bank cycle, so the same holds per row parity).
+    static __device__ __forceinline__ int kx(int r)
+    {
+        return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+    }
     static __device__ __forceinline__ int off(int r, int c) { return r * ROWB + ((c ^ kx(r)) << 4); }
     // Byte address of dim d of row r in that layout.
     static __device__ __forceinline__ int dim_off(int r, int d) { return off(r, d >> 3) + 2 * (d & 7); }
