@@ -365,7 +365,7 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *o, const v
 {
     int st = check_shapes(B, Hq, Hkv, S, D);
     if (st != ATTN_OK) return st;
-    if (B > 65535) return ATTN_EUNSUPPORTED;   // grid z
+    if (((long long)S + 127) / 128 * Hq * (long long)B > 0x7fffffffLL) return ATTN_EUNSUPPORTED;   // dQ grid
     if (window_table != nullptr) return ATTN_EUNSUPPORTED;
     if (causal != 0 && causal != 1) return ATTN_EINVAL;
     if (!std::isfinite(scale) || !(scale > 0.0f)) return ATTN_EINVAL;

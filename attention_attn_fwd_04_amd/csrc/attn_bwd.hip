@@ -149,6 +149,28 @@ __device__ __forceinline__ void stream_tile(u32x4_t rs, uint32_t row_b, int row0
     }
 }
 
+// Work order of the gradient kernels: one work-group per (row tile, head),
+// the tiles with the most streamed work first, over all heads, so the long
+// ones do not start last.  When the heads split evenly over the 8 XCDs
+// (work-groups are dealt to them round robin), XCD x takes heads
+// x * H/8 .. and runs them longest tile first.  Returns the tile rank
+// (0 = most work) and the (batch, head) index, both wave-uniform.
+__device__ __forceinline__ void decode_work(int n_bh, int &rank, int &bh)
+{
+    const int w = blockIdx.x;
+    int r, h;
+    if ((n_bh & 7) == 0) {
+        const int hpx = n_bh >> 3, j = w >> 3;
+        r = j / hpx;
+        h = (w & 7) * hpx + (j - r * hpx);
+    } else {
+        r = w / n_bh;
+        h = w - r * n_bh;
+    }
+    rank = __builtin_amdgcn_readfirstlane(r);
+    bh = __builtin_amdgcn_readfirstlane(h);
+}
+
 // Inverse RoPE of one lane's column of a transposed accumulator (rows = dims
 // 32 db + 8 r + 4 g + j; the pair (d, d + D/2) is (acc[db], acc[db + DB/2])):
 // x = x' c + y' s, y = y' c - x' s with the cosines / sines of position p
@@ -263,8 +285,12 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(const BwdArgs a)
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l32 = lane & 31, g = lane >> 5;
-    const int qt = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
-    const int S = a.S, hk = hq / (a.Hq / a.Hkv);
+    int rank, bh;
+    decode_work(a.B * a.Hq, rank, bh);
+    const int qt = (a.S + kBwdBM - 1) / kBwdBM - 1 - rank;   // the last query tile streams the most keys
+    const int b = __builtin_amdgcn_readfirstlane(bh / a.Hq);
+    const int hq = bh - b * a.Hq;
+    const int S = a.S, hk = __builtin_amdgcn_readfirstlane(hq / (a.Hq / a.Hkv));
     const int n0 = qt * kBwdBM, nw0 = n0 + wave * 32, n = nw0 + l32;
 
     // Resident B operands: the staged query (c R(n) q) and dO of the lane's
@@ -378,7 +404,11 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l32 = lane & 31, g = lane >> 5;
-    const int kt = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+    int rank, bh;
+    decode_work(a.B * a.Hkv, rank, bh);
+    const int kt = CAUSAL ? rank : (a.S + kBwdBM - 1) / kBwdBM - 1 - rank;   // the first key tile streams the most queries
+    const int b = __builtin_amdgcn_readfirstlane(bh / a.Hkv);
+    const int hk = bh - b * a.Hkv;
     const int S = a.S, grp = a.Hq / a.Hkv;
     const int m0 = kt * kBwdBM, mw0 = m0 + wave * 32, m = mw0 + l32;
 
@@ -538,13 +568,13 @@ hipError_t launch_bwd_d(const BwdArgs &a, hipStream_t stream)
                        n_units);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const unsigned tiles = (unsigned)((a.S + kBwdBM - 1) / kBwdBM);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, ROPE>), dim3(tiles, (unsigned)a.Hkv, (unsigned)a.B),
-                       dim3(kBwdThreads), 0, stream, a);
+    const long long tiles = (a.S + kBwdBM - 1) / kBwdBM;
+    const long long n_dkdv = tiles * a.Hkv * a.B, n_dq = tiles * a.Hq * a.B;
+    if (n_dq > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, ROPE>), dim3((unsigned)n_dkdv), dim3(kBwdThreads), 0, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, ROPE>), dim3(tiles, (unsigned)a.Hq, (unsigned)a.B),
-                       dim3(kBwdThreads), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, ROPE>), dim3((unsigned)n_dq), dim3(kBwdThreads), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -216,7 +216,7 @@ _W = (ctypes.c_int32 * 64)(*range(64))
 @pytest.mark.parametrize("kw,status", [
     (dict(w=_W), binding.ATTN_EUNSUPPORTED),           # no backward of the window
     (dict(D=96), binding.ATTN_EUNSUPPORTED),
-    (dict(B=70000), binding.ATTN_EUNSUPPORTED),
+    (dict(B=1_600_000_000, S=256, Hq=1, Hkv=1), binding.ATTN_EUNSUPPORTED),   # dQ grid past 2^31 - 1
     (dict(Hq=5, Hkv=2), binding.ATTN_EINVAL),
     (dict(causal=2), binding.ATTN_EINVAL),
     (dict(scale=-1.0), binding.ATTN_EINVAL),
