@@ -54,8 +54,9 @@
 //    2^14, the common tile needs no max pass, and the 64 multiplies of O are
 //    rare.
 //  * Key tiles are visited from 0 upwards; the masked tiles are the last
-//    ones.  Query tiles are issued longest first, and the block index is
-//    remapped so one head's tiles run on one XCD (shared L2 for its K/V).
+//    ones.  Query tiles are issued longest first within bands of heads, and
+//    the block index is remapped so a band's tiles run on one XCD (shared
+//    L2 for its K/V).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -73,6 +74,7 @@ constexpr int kRowsPerWave = 32;
 constexpr int kBM = kWaves * kRowsPerWave;  // 256 query rows per work-group
 constexpr int kBN = 64;                     // keys per iteration (two 32-key blocks)
 constexpr float kLazyMaxSum = 16384.0f;     // lazy rescale: partial row sums of P stay <= 2^14
+constexpr int kBandTiles = 64;              // query tiles per band of heads in the work order
 
 template <int D, bool ROPE>
 struct Geo {
@@ -125,16 +127,29 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
     const int g = lane >> 5;
 
     // ---- work decode: XCD-contiguous, longest query tile first ----------
+    // Work-groups are dealt to the 8 XCDs round robin; remapped, each XCD
+    // takes a contiguous range of work.  Within it the heads go in bands of
+    // kb heads (about 64 query tiles per band: one head at S = 16k, two at
+    // 8k, eight at 2k), and a band runs its tiles longest first across its
+    // heads.  Few heads in flight per XCD keep their K and V in its L2; a
+    // band of several heads at short S keeps the short tiles of one head
+    // from running alone at its end.
     const int n_qt = (a.S + kBM - 1) / kBM;
-    const int n_work = n_qt * a.Hq * a.B;
+    const int n_bh = a.Hq * a.B;
+    const int n_work = n_qt * n_bh;
     int work = blockIdx.x;
     if ((n_work & 7) == 0)
         work = (blockIdx.x & 7) * (n_work >> 3) + (blockIdx.x >> 3);
+    const int kb = max(1, kBandTiles / n_qt);
+    const int band = work / (kb * n_qt);
+    const int in_band = work - band * kb * n_qt;
+    const int band_heads = min(kb, n_bh - band * kb);
+    const int rank = in_band / band_heads;
     // (readfirstlane: the divisions run on the vector unit; their results are
     // wave-uniform, and everything derived from them can then live in scalar
     // registers, the load descriptors included.)
-    const int bh = __builtin_amdgcn_readfirstlane(work / n_qt);
-    const int qt = __builtin_amdgcn_readfirstlane(n_qt - 1 - (work - bh * n_qt));
+    const int bh = __builtin_amdgcn_readfirstlane(band * kb + (in_band - rank * band_heads));
+    const int qt = __builtin_amdgcn_readfirstlane(n_qt - 1 - rank);
     const int b = __builtin_amdgcn_readfirstlane(bh / a.Hq);
     const int hq = bh - b * a.Hq;
     const int hk = __builtin_amdgcn_readfirstlane(hq / (a.Hq / a.Hkv));
