@@ -218,6 +218,22 @@ void decode_plan(int B, int Hkv, int L, int num_splits, int *n_split, int *keys_
     *n_split = (L + kps - 1) / kps;
 }
 
+// Work-groups of attn_bwd's dK/dV kernel per (128-key tile, KV head): the
+// group's query heads are split over separate work-groups (fp32 partial sums,
+// then a reduction) when the unsplit grid would be under four rounds of
+// resident work-groups (2 per CU on 256 CUs): its longest work-group, the
+// first key tile walking every query tile of every head of the group, would
+// otherwise set the kernel's end.
+int bwd_split(int B, int Hq, int Hkv, int S)
+{
+    const int grp = Hq / Hkv;
+    if (grp <= 1) return 1;
+    const long long grid = ((long long)S + 127) / 128 * Hkv * (long long)B;
+    return grid < 4 * 512 ? grp : 1;
+}
+
+size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+
 }  // namespace
 
 extern "C" {
@@ -349,14 +365,18 @@ int attn_decode(const void *q, const void *k, const void *v, void *o, float *lse
     return ATTN_OK;
 }
 
-// Workspace of attn_bwd: the staged queries, the staged keys, then Delta,
-// each section 256-byte aligned.
+
+// Workspace of attn_bwd: the staged queries, the staged keys, Delta, then
+// (split dK/dV only) the fp32 partial dK and dV, each section 256-byte
+// aligned.
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D)
 {
-    if (B <= 0 || S <= 0 || Hq < 1 || Hkv < 1 || D <= 0) return 0;
-    const size_t qs = ((size_t)B * S * Hq * D * 2 + 255) / 256 * 256;
-    const size_t kr = ((size_t)B * S * Hkv * D * 2 + 255) / 256 * 256;
-    return qs + kr + (size_t)B * Hq * S * 4;
+    if (B <= 0 || S <= 0 || Hq < 1 || Hkv < 1 || D <= 0 || Hq % Hkv != 0) return 0;
+    size_t n = align256((size_t)B * S * Hq * D * 2) + align256((size_t)B * S * Hkv * D * 2) +
+               align256((size_t)B * Hq * S * 4);
+    const int split = bwd_split(B, Hq, Hkv, S);
+    if (split > 1) n += 2 * align256((size_t)split * B * S * Hkv * D * 4);
+    return n;
 }
 
 int attn_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout, const float *lse,
@@ -408,10 +428,16 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *o, const v
     a.dk = static_cast<uint16_t *>(dk);
     a.dv = static_cast<uint16_t *>(dv);
     uint8_t *ws = static_cast<uint8_t *>(workspace);
-    const size_t qs_b = (nq + 255) / 256 * 256, kr_b = (nkv + 255) / 256 * 256;
+    const size_t qs_b = align256(nq), kr_b = align256(nkv), dl_b = align256((size_t)B * Hq * S * 4);
     a.qs = reinterpret_cast<uint16_t *>(ws);
     a.kr = reinterpret_cast<uint16_t *>(ws + qs_b);
     a.delta = reinterpret_cast<float *>(ws + qs_b + kr_b);
+    a.split = bwd_split(B, Hq, Hkv, S);
+    if (a.split > 1) {
+        const size_t part_b = align256((size_t)a.split * B * S * Hkv * D * 4);
+        a.part_dk = reinterpret_cast<float *>(ws + qs_b + kr_b + dl_b);
+        a.part_dv = reinterpret_cast<float *>(ws + qs_b + kr_b + dl_b + part_b);
+    }
     a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.S = S; a.D = D;
     a.causal = causal;
     a.scale = scale;

@@ -30,7 +30,12 @@
 //    products need (P, dS), as in the forward kernel.  Each score chain
 //    starts from -L log2 e, so P = exp2(accumulator).
 //  * With grouped heads the dK/dV kernel walks the group's query heads in
-//    turn, accumulating into the same registers.
+//    turn, accumulating into the same registers.  When its grid is short
+//    (under four rounds of resident work-groups), each (key tile, KV head)
+//    is split into one work-group per query head instead: the first key
+//    tile would otherwise stream every query tile of every head of the
+//    group alone and set the kernel's end.  The splits write fp32 partial
+//    sums, and a reduction kernel adds them in a fixed order (no atomics).
 //  * Both gradient kernels fit 256 registers per lane, so two waves share
 //    each SIMD (two work-groups per CU): one wave's LDS waits and softmax
 //    arithmetic overlap the other's MFMAs.
@@ -210,6 +215,18 @@ __device__ __forceinline__ void store_acc(uint16_t *row, const f32x16_t (&acc)[D
             w.y = pack_bf16x2(acc[db][4 * r + 2] * k, acc[db][4 * r + 3] * k);
             *reinterpret_cast<uint2 *>(row + db * 32 + 8 * r + 4 * g) = w;
         }
+}
+
+// The same column as fp32, times k (partial sums of a split dK/dV).
+template <int D>
+__device__ __forceinline__ void store_acc_f32(float *row, const f32x16_t (&acc)[D / 32], float k, int g)
+{
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            *reinterpret_cast<float4 *>(row + db * 32 + 8 * r + 4 * g) =
+                make_float4(acc[db][4 * r] * k, acc[db][4 * r + 1] * k, acc[db][4 * r + 2] * k, acc[db][4 * r + 3] * k);
 }
 
 // ---- preprocessing --------------------------------------------------------
@@ -404,12 +421,15 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l32 = lane & 31, g = lane >> 5;
-    int rank, bh;
-    decode_work(a.B * a.Hkv, rank, bh);
+    int rank, bhs;
+    decode_work(a.B * a.Hkv * a.split, rank, bhs);
     const int kt = CAUSAL ? rank : (a.S + kBwdBM - 1) / kBwdBM - 1 - rank;   // the first key tile streams the most queries
+    const int bh = __builtin_amdgcn_readfirstlane(bhs / a.split);
+    const int sp = bhs - bh * a.split;   // which share of the group's query heads
     const int b = __builtin_amdgcn_readfirstlane(bh / a.Hkv);
     const int hk = bh - b * a.Hkv;
-    const int S = a.S, grp = a.Hq / a.Hkv;
+    const int S = a.S, grp = a.Hq / a.Hkv / a.split;   // query heads walked by this work-group
+    const int hq0 = hk * (a.Hq / a.Hkv) + sp * grp;
     const int m0 = kt * kBwdBM, mw0 = m0 + wave * 32, m = mw0 + l32;
 
     // Resident B operands: K' and V of the lane's key (buffer loads: zero
@@ -432,7 +452,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
     const uint32_t smem32 = lds_addr(smem);
     auto qslot = [&](int u) { return smem32 + (uint32_t)((u & 1) * 2 * G::TILE_B); };
     auto dslot = [&](int u) { return smem32 + (uint32_t)((u & 1) * 2 * G::TILE_B + G::TILE_B); };
-    // Streamed tiles u = 0 .. U-1: query head hk grp + u / nt, query tile
+    // Streamed tiles u = 0 .. U-1: query head hq0 + u / nt, query tile
     // t0 + u % nt (causal: from the first tile that reaches this key tile).
     const int t0 = CAUSAL ? m0 / kBwdBN : 0;
     const int nt = (S + kBwdBN - 1) / kBwdBN - t0;
@@ -443,7 +463,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
     float pre_l = 0.f, pre_d = 0.f;
     auto rows_fetch = [&](int u) {
         if (wave == 0 && lane < kBwdBN) {
-            const int hq = hk * grp + u / nt, nq = (t0 + u % nt) * kBwdBN + lane;
+            const int hq = hq0 + u / nt, nq = (t0 + u % nt) * kBwdBN + lane;
             const size_t rowid = ((size_t)b * a.Hq + hq) * S + nq;
             pre_l = nq < S ? a.lse[rowid] * kLog2e : 0.f;
             pre_d = nq < S ? a.delta[rowid] : 0.f;
@@ -456,7 +476,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
         }
     };
     auto load = [&](int u) {
-        const int hq = hk * grp + u / nt, t = t0 + u % nt;
+        const int hq = hq0 + u / nt, t = t0 + u % nt;
         const u32x4_t q_rs = make_desc(a.qs + ((size_t)b * S * a.Hq + hq) * D, (uint32_t)S * q_rowb);
         const u32x4_t d_rs = make_desc(a.dout + ((size_t)b * S * a.Hq + hq) * D, (uint32_t)S * q_rowb);
         stream_tile<D>(q_rs, q_rowb, t * kBwdBN, qslot(u), wave, lane);
@@ -550,10 +570,34 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
         __builtin_amdgcn_sched_barrier(0);
     }
     if (m >= S) return;
-    store_acc<D>(a.dv + koff, dv, 1.0f, g);
     if constexpr (ROPE) unrotate_acc<D>(dk, a.rope_cs, m, g);
     // The streamed queries carry c = scale log2 e: dK' = scale dS^T Q' = (scale / c) dS^T (c Q').
-    store_acc<D>(a.dk + koff, dk, a.scale / a.scale_log2e, g);
+    const float kscale = a.scale / a.scale_log2e;
+    if (a.split == 1) {
+        store_acc<D>(a.dv + koff, dv, 1.0f, g);
+        store_acc<D>(a.dk + koff, dk, kscale, g);
+    } else {
+        const size_t poff = (size_t)sp * a.B * S * a.Hkv * D + koff;
+        store_acc_f32<D>(a.part_dv + poff, dv, 1.0f, g);
+        store_acc_f32<D>(a.part_dk + poff, dk, kscale, g);
+    }
+}
+
+// ---- sum of the split dK/dV partials: one thread per 4 values ---------------
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(const BwdArgs a, long long n4)
+{
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n4) return;
+    const size_t stride = (size_t)a.B * a.S * a.Hkv * a.D;
+    float4 sk = make_float4(0.f, 0.f, 0.f, 0.f), sv = sk;
+    for (int s = 0; s < a.split; ++s) {
+        const float4 pk = reinterpret_cast<const float4 *>(a.part_dk + s * stride)[i];
+        const float4 pv = reinterpret_cast<const float4 *>(a.part_dv + s * stride)[i];
+        sk.x += pk.x; sk.y += pk.y; sk.z += pk.z; sk.w += pk.w;
+        sv.x += pv.x; sv.y += pv.y; sv.z += pv.z; sv.w += pv.w;
+    }
+    reinterpret_cast<uint2 *>(a.dk)[i] = make_uint2(pack_bf16x2(sk.x, sk.y), pack_bf16x2(sk.z, sk.w));
+    reinterpret_cast<uint2 *>(a.dv)[i] = make_uint2(pack_bf16x2(sv.x, sv.y), pack_bf16x2(sv.z, sv.w));
 }
 
 template <int D, bool CAUSAL, bool ROPE>
@@ -569,11 +613,17 @@ hipError_t launch_bwd_d(const BwdArgs &a, hipStream_t stream)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const long long tiles = (a.S + kBwdBM - 1) / kBwdBM;
-    const long long n_dkdv = tiles * a.Hkv * a.B, n_dq = tiles * a.Hq * a.B;
-    if (n_dq > 0x7fffffffLL) return hipErrorInvalidValue;
+    const long long n_dkdv = tiles * a.Hkv * a.B * a.split, n_dq = tiles * a.Hq * a.B;
+    if (n_dq > 0x7fffffffLL || n_dkdv > 0x7fffffffLL) return hipErrorInvalidValue;
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, ROPE>), dim3((unsigned)n_dkdv), dim3(kBwdThreads), 0, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (a.split > 1) {
+        const long long n4 = (long long)a.B * a.S * a.Hkv * D / 4;
+        hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream, a, n4);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, ROPE>), dim3((unsigned)n_dq), dim3(kBwdThreads), 0, stream, a);
     return hipGetLastError();
 }

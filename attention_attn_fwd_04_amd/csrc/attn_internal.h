@@ -78,6 +78,9 @@ struct BwdArgs {
     uint16_t *kr;             // workspace [B, S, Hkv, D]: bf16(R(m) k); unused without RoPE
     const uint16_t *kop;      // the K operand: kr with RoPE, k without
     float *delta;             // workspace [B, Hq, S]: rowsum(dO o O)
+    float *part_dk;           // workspace [split, B, S, Hkv, D] fp32 partial dK, dV when split > 1
+    float *part_dv;
+    int split;                // dK/dV work-groups per (key tile, KV head), each over Hq/Hkv/split query heads
     const uint16_t *rope_cs;  // fp16 cos/sin table; null when RoPE is off
     int B, Hq, Hkv, S, D;
     int causal;

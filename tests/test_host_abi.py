@@ -191,12 +191,25 @@ def test_decode_empty_is_ok_without_device():
 
 def test_bwd_workspace_bytes():
     """Staged queries and keys (bf16) and Delta (fp32), 256-byte aligned
-    sections; 0 for empty or invalid sizes."""
+    sections, plus fp32 partial dK and dV per query head of a group when the
+    dK/dV grid (one work-group per 128 keys and KV head) is under 2048
+    work-groups; 0 for empty or invalid sizes."""
     ws = binding.attn_bwd_workspace_bytes
     assert ws(0, 8, 2, 100, 128) == 0 and ws(1, 8, 2, 0, 128) == 0 and ws(1, 0, 2, 10, 128) == 0
+    assert ws(1, 8, 3, 100, 128) == 0
+    base = lambda B, Hq, Hkv, S, D: B * S * Hq * D * 2 + B * S * Hkv * D * 2 + B * Hq * S * 4
+    # split: 8 tiles x 2 KV heads x 2 = 32 work-groups, each group of 4 heads split in 4
     B, Hq, Hkv, S, D = 2, 8, 2, 1000, 128
-    need = B * S * Hq * D * 2 + B * S * Hkv * D * 2 + B * Hq * S * 4
-    assert need <= ws(B, Hq, Hkv, S, D) <= need + 512
+    need = base(B, Hq, Hkv, S, D) + 2 * 4 * B * S * Hkv * D * 4
+    assert need <= ws(B, Hq, Hkv, S, D) <= need + 1280
+    # not split: 64 tiles x 8 KV heads x 4 = 2048 work-groups
+    B, Hq, Hkv, S, D = 4, 32, 8, 8192, 128
+    need = base(B, Hq, Hkv, S, D)
+    assert need <= ws(B, Hq, Hkv, S, D) <= need + 768
+    # no groups, never split
+    B, Hq, Hkv, S, D = 1, 2, 2, 300, 64
+    need = base(B, Hq, Hkv, S, D)
+    assert need <= ws(B, Hq, Hkv, S, D) <= need + 768
 
 
 def _bwd_call(**kw):
