@@ -15,6 +15,7 @@
 #include <vector>
 
 #include "attn_internal.h"
+#include "attn_ext_args.h"
 
 namespace {
 

@@ -44,6 +44,7 @@
 
 #include "attn_gfx950.h"
 #include "attn_internal.h"
+#include "attn_ext_args.h"
 
 namespace attn {
 namespace {

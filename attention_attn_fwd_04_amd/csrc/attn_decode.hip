@@ -38,6 +38,7 @@
 
 #include "attn_gfx950.h"
 #include "attn_internal.h"
+#include "attn_ext_args.h"
 
 namespace attn {
 namespace {

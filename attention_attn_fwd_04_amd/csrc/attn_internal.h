@@ -45,55 +45,11 @@ struct RopeArgs {
     int B, Hq, Hkv, S, D;
 };
 
-// Most splits of one decode: the merge keeps one weight per split in LDS.
-constexpr int kMaxDecodeSplits = 1024;
-
-struct DecodeArgs {
-    const uint16_t *q;        // [B, Hq, D]
-    const uint16_t *k;        // [B, L, Hkv, D] cache
-    const uint16_t *v;
-    uint16_t *o;              // [B, Hq, D]
-    const uint16_t *rope_cs;  // fp16 cos/sin table (positions 0..L-1); null when RoPE is off
-    float *lse;               // [B, Hq] or null
-    float *part_o;            // [B, Hq, n_split, D] partial (unnormalised) outputs
-    float *part_ml;           // [B, Hq, n_split, 2] partial (m, l)
-    int B, Hq, Hkv, L, D;
-    int n_split, keys_per_split;
-    int use_window;
-    float scale_log2e;
-    int32_t window[kMaxPairs];
-};
-
-struct BwdArgs {
-    const uint16_t *q;        // [B, S, Hq, D]
-    const uint16_t *k;        // [B, S, Hkv, D]
-    const uint16_t *v;
-    const uint16_t *o;        // forward output [B, S, Hq, D]
-    const uint16_t *dout;     // dL/dO [B, S, Hq, D]
-    const float *lse;         // [B, Hq, S] natural-log LSE of the forward's rows
-    uint16_t *dq;             // [B, S, Hq, D]
-    uint16_t *dk;             // [B, S, Hkv, D]
-    uint16_t *dv;
-    uint16_t *qs;             // workspace [B, S, Hq, D]: bf16(scale log2e R(n) q)
-    uint16_t *kr;             // workspace [B, S, Hkv, D]: bf16(R(m) k); unused without RoPE
-    const uint16_t *kop;      // the K operand: kr with RoPE, k without
-    float *delta;             // workspace [B, Hq, S]: rowsum(dO o O)
-    float *part_dk;           // workspace [split, B, S, Hkv, D] fp32 partial dK, dV when split > 1
-    float *part_dv;
-    int split;                // dK/dV work-groups per (key tile, KV head), each over Hq/Hkv/split query heads
-    const uint16_t *rope_cs;  // fp16 cos/sin table; null when RoPE is off
-    int B, Hq, Hkv, S, D;
-    int causal;
-    float scale;
-    float scale_log2e;
-};
-
-// Launchers (attn_fwd_kernel.hip, rope_pass.hip, attn_decode.hip,
-// attn_bwd.hip).  Return hipSuccess or the launch error.
+// Launchers (attn_fwd_kernel.hip, rope_pass.hip).  Return hipSuccess or the
+// launch error.  The decode and backward launchers are declared in
+// attn_ext_args.h.
 hipError_t launch_attn_fwd(const FwdArgs &a, hipStream_t stream);
 hipError_t launch_rope_pass(const RopeArgs &a, hipStream_t stream);
-hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
-hipError_t launch_attn_bwd(const BwdArgs &a, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
 // Device helpers used by both the fused kernel and the separate RoPE pass, so
