@@ -222,9 +222,8 @@ void decode_plan(int B, int Hkv, int L, int num_splits, int *n_split, int *keys_
 // Work-groups of attn_bwd's dK/dV kernel per (128-key tile, KV head): the
 // group's query heads are split over separate work-groups (fp32 partial sums,
 // then a reduction) when the unsplit grid would be under four rounds of
-// resident work-groups (2 per CU on 256 CUs): its longest work-group, the
-// first key tile walking every query tile of every head of the group, would
-// otherwise set the kernel's end.
+// resident work-groups (2 per CU on 256 CUs); the finer work-groups balance
+// better over the CUs.
 int bwd_split(int B, int Hq, int Hkv, int S)
 {
     const int grp = Hq / Hkv;

@@ -32,9 +32,9 @@
 //  * With grouped heads the dK/dV kernel walks the group's query heads in
 //    turn, accumulating into the same registers.  When its grid is short
 //    (under four rounds of resident work-groups), each (key tile, KV head)
-//    is split into one work-group per query head instead: the first key
-//    tile would otherwise stream every query tile of every head of the
-//    group alone and set the kernel's end.  The splits write fp32 partial
+//    is split into one work-group per query head instead, four times as
+//    many shorter work-groups, which balance better over the CUs (measured
+//    faster on the grouped-head workload).  The splits write fp32 partial
 //    sums, and a reduction kernel adds them in a fixed order (no atomics).
 //  * Both gradient kernels fit 256 registers per lane, so two waves share
 //    each SIMD (two work-groups per CU): one wave's LDS waits and softmax
