@@ -219,17 +219,17 @@ void decode_plan(int B, int Hkv, int L, int num_splits, int *n_split, int *keys_
     *n_split = (L + kps - 1) / kps;
 }
 
-// Work-groups of attn_bwd's dK/dV kernel per (128-key tile, KV head): the
+// Work-groups of attn_bwd's dK/dV kernel per (256-key tile, KV head): the
 // group's query heads are split over separate work-groups (fp32 partial sums,
 // then a reduction) when the unsplit grid would be under four rounds of
-// resident work-groups (2 per CU on 256 CUs); the finer work-groups balance
+// resident work-groups (1 per CU on 256 CUs); the finer work-groups balance
 // better over the CUs.
 int bwd_split(int B, int Hq, int Hkv, int S)
 {
     const int grp = Hq / Hkv;
     if (grp <= 1) return 1;
-    const long long grid = ((long long)S + 127) / 128 * Hkv * (long long)B;
-    return grid < 4 * 512 ? grp : 1;
+    const long long grid = ((long long)S + 255) / 256 * Hkv * (long long)B;
+    return grid < 4 * 256 ? grp : 1;
 }
 
 size_t align256(size_t n) { return (n + 255) / 256 * 256; }
@@ -385,7 +385,6 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *o, const v
 {
     int st = check_shapes(B, Hq, Hkv, S, D);
     if (st != ATTN_OK) return st;
-    if (((long long)S + 127) / 128 * Hq * (long long)B > 0x7fffffffLL) return ATTN_EUNSUPPORTED;   // dQ grid
     if (window_table != nullptr) return ATTN_EUNSUPPORTED;
     if (causal != 0 && causal != 1) return ATTN_EINVAL;
     if (!std::isfinite(scale) || !(scale > 0.0f)) return ATTN_EINVAL;

@@ -18,10 +18,11 @@
 //    bf16(scale log2e R(n) q), rounded once exactly as the forward kernel
 //    stages it, and K as bf16(R(m) k), bitwise the forward's K'.  Scores
 //    then come out of the MFMAs in the exp2 domain.
-//  * Work-groups of 4 waves own 128 rows (32 per wave): queries in the dQ
+//  * Work-groups of 8 waves own 256 rows (32 per wave): queries in the dQ
 //    kernel, keys in the dK/dV kernel.  The other side streams through LDS
 //    in 32-row tiles (direct-to-LDS buffer loads, two slots, the next tile
-//    loading while the current one is used), one barrier per tile.
+//    loading while the current one is used), one barrier per tile; each
+//    streamed tile feeds all 8 waves.
 //  * All products are 32x32x16 bf16 MFMAs with fp32 accumulation.  The
 //    operands that stay (Q and dO for dQ; K' and V for dK, dV) sit in
 //    B-operand registers; the streamed tile gives A operands, as 16-byte
@@ -37,8 +38,8 @@
 //    faster on the grouped-head workload).  The splits write fp32 partial
 //    sums, and a reduction kernel adds them in a fixed order (no atomics).
 //  * Both gradient kernels fit 256 registers per lane, so two waves share
-//    each SIMD (two work-groups per CU): one wave's LDS waits and softmax
-//    arithmetic overlap the other's MFMAs.
+//    each SIMD: one wave's LDS waits and softmax arithmetic overlap the
+//    other's MFMAs.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -49,7 +50,7 @@
 namespace attn {
 namespace {
 
-constexpr int kBwdWaves = 4;
+constexpr int kBwdWaves = 8;
 constexpr int kBwdThreads = kBwdWaves * 64;
 constexpr int kBwdBM = kBwdWaves * 32;   // rows per work-group
 constexpr int kBwdBN = 32;               // rows per streamed tile
@@ -64,9 +65,9 @@ struct BGeo {
     static constexpr int ROWB = 2 * D;
     static constexpr int TILE_B = kBwdBN * ROWB;
     static constexpr int NI = TILE_B / 1024;
-    static constexpr int NI_W = NI / kBwdWaves;
+    static constexpr int NI_W = NI >= kBwdWaves ? NI / kBwdWaves : 1;
     static constexpr int RPI = 1024 / ROWB;
-    static_assert(NI % kBwdWaves == 0, "direct loads split over the waves");
+    static_assert(NI % kBwdWaves == 0 || kBwdWaves % NI == 0, "direct loads split over the waves");
     // 16-byte chunks XOR-permuted per row.  The streamed tiles are read both
     // as rows (ds_read_b128: 16 lanes, 16 consecutive rows, one logical
     // chunk) and transposed (ds_read_b64_tr_b16: 32 lanes, 4 consecutive rows
@@ -150,6 +151,7 @@ __device__ __forceinline__ void stream_tile(u32x4_t rs, uint32_t row_b, int row0
 #pragma unroll
     for (int i = 0; i < G::NI_W; ++i) {
         const int ins = wave + kBwdWaves * i;
+        if (ins >= G::NI) break;   // D = 64: fewer load instructions than waves (wave-uniform)
         const int r = ins * G::RPI + dl_row;
         dma16(rs, (uint32_t)(row0 + r) * row_b + 16u * (uint32_t)(dl_slot ^ G::kx(r)), lds_dst + (uint32_t)(ins * 1024));
     }

@@ -162,9 +162,9 @@ int attn_decode(const void *q, const void *k, const void *v, void *o, float *lse
  *      attn_bwd_workspace_bytes(B, Hq, Hkv, S, D) bytes, 16-byte aligned
  *      (staged operands and Delta); contents on entry do not matter.
  *  window_table must be NULL (the backward of the per-pair window is not
- *      built: ATTN_EUNSUPPORTED).  ceil(S/128)·Hq·B must not exceed 2^31 - 1
- *      (one work-group per 128 query rows and head; ATTN_EUNSUPPORTED).
- *      Other arguments and errors as for attn_fwd.
+ *      built: ATTN_EUNSUPPORTED).  Other arguments, size limits and errors as
+ *      for attn_fwd (the gradient grids have at most one work-group per 256
+ *      rows and query head, within attn_fwd's bound).
  */
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D);
 int attn_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,

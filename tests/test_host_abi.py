@@ -192,17 +192,17 @@ def test_decode_empty_is_ok_without_device():
 def test_bwd_workspace_bytes():
     """Staged queries and keys (bf16) and Delta (fp32), 256-byte aligned
     sections, plus fp32 partial dK and dV per query head of a group when the
-    dK/dV grid (one work-group per 128 keys and KV head) is under 2048
+    dK/dV grid (one work-group per 256 keys and KV head) is under 1024
     work-groups; 0 for empty or invalid sizes."""
     ws = binding.attn_bwd_workspace_bytes
     assert ws(0, 8, 2, 100, 128) == 0 and ws(1, 8, 2, 0, 128) == 0 and ws(1, 0, 2, 10, 128) == 0
     assert ws(1, 8, 3, 100, 128) == 0
     base = lambda B, Hq, Hkv, S, D: B * S * Hq * D * 2 + B * S * Hkv * D * 2 + B * Hq * S * 4
-    # split: 8 tiles x 2 KV heads x 2 = 32 work-groups, each group of 4 heads split in 4
+    # split: 4 tiles x 2 KV heads x 2 = 16 work-groups, each group of 4 heads split in 4
     B, Hq, Hkv, S, D = 2, 8, 2, 1000, 128
     need = base(B, Hq, Hkv, S, D) + 2 * 4 * B * S * Hkv * D * 4
     assert need <= ws(B, Hq, Hkv, S, D) <= need + 1280
-    # not split: 64 tiles x 8 KV heads x 4 = 2048 work-groups
+    # not split: 32 tiles x 8 KV heads x 4 = 1024 work-groups
     B, Hq, Hkv, S, D = 4, 32, 8, 8192, 128
     need = base(B, Hq, Hkv, S, D)
     assert need <= ws(B, Hq, Hkv, S, D) <= need + 768
@@ -229,7 +229,7 @@ _W = (ctypes.c_int32 * 64)(*range(64))
 @pytest.mark.parametrize("kw,status", [
     (dict(w=_W), binding.ATTN_EUNSUPPORTED),           # no backward of the window
     (dict(D=96), binding.ATTN_EUNSUPPORTED),
-    (dict(B=1_600_000_000, S=256, Hq=1, Hkv=1), binding.ATTN_EUNSUPPORTED),   # dQ grid past 2^31 - 1
+    (dict(B=1_600_000_000, S=512, Hq=1, Hkv=1), binding.ATTN_EINVAL),   # over 2^31 - 1 work-groups
     (dict(Hq=5, Hkv=2), binding.ATTN_EINVAL),
     (dict(causal=2), binding.ATTN_EINVAL),
     (dict(scale=-1.0), binding.ATTN_EINVAL),
