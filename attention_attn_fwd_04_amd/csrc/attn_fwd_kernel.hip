@@ -235,41 +235,43 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
     // each 1 KB = RPI rows; lane l writes chunk slot l % CH of row l / CH, i.e.
     // the global chunk (slot ^ swizzle(row)).  Rows are keys (K, V) or
     // positions (the cos/sin table, whose rows have the K row geometry).
+    // A load's byte offset is the lane's part (row within the tile, swizzled
+    // chunk), computed once here, plus the tile's row offset, a wave-uniform
+    // product added per load: one vector add instead of a 32-bit multiply.
     const int dl_row = lane / G::CH, dl_slot = lane % G::CH;
-    auto dload = [&](u32x4_t rs, uint32_t rowb, uint32_t dst, int t, bool vlayout)
+    uint32_t lane_v[G::NI_W], lane_k[G::NI_W], lane_c[G::NI_W];
+#pragma unroll
+    for (int j = 0; j < G::NI_W; ++j) {
+        const int r = (wave + kWaves * j) * G::RPI + dl_row;
+        lane_v[j] = (uint32_t)r * kv_rowb + 16u * (uint32_t)(dl_slot ^ G::vx(r));
+        lane_k[j] = (uint32_t)r * kv_rowb + 16u * (uint32_t)(dl_slot ^ G::kx(r));
+        lane_c[j] = (uint32_t)r * (uint32_t)G::ROWB + 16u * (uint32_t)(dl_slot ^ G::kx(r));
+    }
+    auto dload = [&](u32x4_t rs, uint32_t rowb, uint32_t dst, int t, const uint32_t (&lane_off)[G::NI_W])
         __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < G::NI_W; ++i) {
-            const int ins = wave + kWaves * i;
-            const int r = ins * G::RPI + dl_row;
-            const int sw = vlayout ? G::vx(r) : G::kx(r);
-            const uint32_t off = (uint32_t)(t * kBN + r) * rowb + 16u * (uint32_t)(dl_slot ^ sw);
-            dma16(rs, off, dst + (uint32_t)(ins * 1024));
-        }
+        for (int j = 0; j < G::NI_W; ++j)
+            dma16(rs, (uint32_t)(t * kBN) * rowb + lane_off[j], dst + (uint32_t)((wave + kWaves * j) * 1024));
     };
     auto dload_k = [&](int t) __attribute__((always_inline)) {
-        dload(k_rs, kv_rowb, kslot32(t), t, false);
-        if constexpr (ROPE) dload(cs_desc, (uint32_t)G::ROWB, cslot32(t), t, false);
+        dload(k_rs, kv_rowb, kslot32(t), t, lane_k);
+        if constexpr (ROPE) dload(cs_desc, (uint32_t)G::ROWB, cslot32(t), t, lane_c);
     };
-    auto dload_v = [&](int t) __attribute__((always_inline)) { dload(v_rs, kv_rowb, vslot32(t), t, true); };
+    auto dload_v = [&](int t) __attribute__((always_inline)) { dload(v_rs, kv_rowb, vslot32(t), t, lane_v); };
     // Loads of iteration i, one 1 KB instruction per step: V(i+1), K(i+3)
     // and, with RoPE, the cos/sin rows of K(i+3).  They are issued in every
     // iteration: tiles past the end read as zeros into slots that are free
     // and never read again, which keeps the wait counts constant.
     constexpr int NDMA = G::NI_W * (ROPE ? 3 : 2);
     auto dma_step = [&](int i, int j) __attribute__((always_inline)) {
-        const int which = j / G::NI_W, ins = wave + kWaves * (j % G::NI_W);
-        const int r = ins * G::RPI + dl_row;
-        if (which == 0) {
-            const uint32_t off = (uint32_t)((i + 1) * kBN + r) * kv_rowb + 16u * (uint32_t)(dl_slot ^ G::vx(r));
-            dma16(v_rs, off, vslot32(i + 1) + (uint32_t)(ins * 1024));
-        } else if (which == 1) {
-            const uint32_t off = (uint32_t)((i + 3) * kBN + r) * kv_rowb + 16u * (uint32_t)(dl_slot ^ G::kx(r));
-            dma16(k_rs, off, kslot32(i + 3) + (uint32_t)(ins * 1024));
-        } else {
-            const uint32_t off = (uint32_t)((i + 3) * kBN + r) * (uint32_t)G::ROWB + 16u * (uint32_t)(dl_slot ^ G::kx(r));
-            dma16(cs_desc, off, cslot32(i + 3) + (uint32_t)(ins * 1024));
-        }
+        const int which = j / G::NI_W, jj = j % G::NI_W;
+        const uint32_t dst = (uint32_t)((wave + kWaves * jj) * 1024);
+        if (which == 0)
+            dma16(v_rs, (uint32_t)((i + 1) * kBN) * kv_rowb + lane_v[jj], vslot32(i + 1) + dst);
+        else if (which == 1)
+            dma16(k_rs, (uint32_t)((i + 3) * kBN) * kv_rowb + lane_k[jj], kslot32(i + 3) + dst);
+        else
+            dma16(cs_desc, (uint32_t)((i + 3) * kBN) * (uint32_t)G::ROWB + lane_c[jj], cslot32(i + 3) + dst);
     };
 
     // RoPE: lane l of wave w rotates unit (key l, pair group w) of
@@ -350,7 +352,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
     };
 
     // P = 2^(s c - m_ref) of one (masked) tile (s the accumulator: already
-    // shifted), packed into pf; returns the lane's partial row sum.
+    // shifted), packed into pf; returns the lane's partial row sum (of the
+    // fp32 P, before the bf16 rounding for the PV operand).
     auto exp_tile = [&](const f32x16_t (&s)[2], bf16x8_t (&pf)[kBN / 16]) __attribute__((always_inline)) {
         float r0 = 0.f, r1 = 0.f;
 #pragma unroll
@@ -361,9 +364,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
             for (int e = 0; e < 8; ++e) p[e] = fast_exp2(s[kb][h8 + e]);
             uint32_t w[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(p[2 * e], p[2 * e + 1]);
-            r0 = sum_bf16x2(w[0], sum_bf16x2(w[2], r0));
-            r1 = sum_bf16x2(w[1], sum_bf16x2(w[3], r1));
+            for (int e = 0; e < 4; ++e) {
+                w[e] = pack_bf16x2(p[2 * e], p[2 * e + 1]);
+                r0 += p[2 * e];
+                r1 += p[2 * e + 1];
+            }
             pf[ch] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
         }
         return r0 + r1;
@@ -588,8 +593,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
     };
 
     // Block 2: O^T += V(i-1)^T P(i-1)^T from pp; with EXP, P(i) = 2^(S(i) c
-    // - m_ref) into pn, two scores per step, 32 steps spread over the MFMAs.
-    // Returns the lane's partial row sum of P(i).
+    // - m_ref) into pn, two scores per step, 16 steps spread over the MFMAs.
+    // Returns the lane's partial row sum of P(i) (fp32, before rounding).
     auto block2 = [&](auto exp_c, int i, const bf16x8_t (&pp)[kBN / 16], bf16x8_t (&pn)[kBN / 16])
         __attribute__((always_inline)) {
         constexpr bool EXP = decltype(exp_c)::value;
@@ -609,16 +614,29 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
         };
         float r[4] = {0.f, 0.f, 0.f, 0.f};
         uint32_t w[16];
-        // Step e: scores 2e, 2e+1 in P order (chunk e / 4, word e % 4).
-        // The empty volatile asm statement pins each step before the next
-        // fence (without it the arithmetic is sunk below the last MFMA).
+        float pe[16][2];
+        // Step e (0 .. 17) of the softmax chain, software-pipelined so that no
+        // instruction waits on the one just before it: the exps of pair e
+        // (scores 2e, 2e+1 in P order: chunk e / 4, word e % 4), the bf16
+        // packing of pair e-1, the fp32 row-sum adds of pair e-2.  The empty
+        // volatile asm statements pin each step before the next fence
+        // (without them the arithmetic is sunk below the last MFMA).
         auto exp_step = [&](int e) __attribute__((always_inline)) {
-            const int ch = e >> 2, kb = ch >> 1, h = (ch & 1) * 8 + 2 * (e & 3);
-            const float p0 = fast_exp2(sc[kb][h]);
-            const float p1 = fast_exp2(sc[kb][h + 1]);
-            w[e] = pack_bf16x2(p0, p1);
-            r[e & 3] = sum_bf16x2(w[e], r[e & 3]);
-            asm volatile("" : "+v"(w[e]), "+v"(r[e & 3]));
+            if (e < 16) {
+                const int ch = e >> 2, kb = ch >> 1, h = (ch & 1) * 8 + 2 * (e & 3);
+                pe[e][0] = fast_exp2(sc[kb][h]);
+                pe[e][1] = fast_exp2(sc[kb][h + 1]);
+                asm volatile("" : "+v"(pe[e][0]), "+v"(pe[e][1]));
+            }
+            if (e >= 1 && e <= 16) {
+                w[e - 1] = pack_bf16x2(pe[e - 1][0], pe[e - 1][1]);
+                asm volatile("" : "+v"(w[e - 1]));
+            }
+            if (e >= 2) {
+                r[(e - 2) & 1] += pe[e - 2][0];
+                r[2 + ((e - 2) & 1)] += pe[e - 2][1];
+                asm volatile("" : "+v"(r[(e - 2) & 1]), "+v"(r[2 + ((e - 2) & 1)]));
+            }
         };
 #pragma unroll
         for (int k = 0; k < PF; ++k) vread(k);
@@ -631,9 +649,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
             const bf16x8_t va = __builtin_bit_cast(bf16x8_t, make_uint4(u0.x, u0.y, u1.x, u1.y));
             acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pp[ch], acc_o[db], 0, 0, 0);
             if constexpr (EXP) {
-                constexpr int PER = 16 / NM2;   // exp steps per MFMA
+                constexpr int PER = 16 / NM2;   // exp steps per MFMA; the last MFMA also drains the chain
 #pragma unroll
                 for (int q = 0; q < PER; ++q) exp_step(k * PER + q);
+                if (k == NM2 - 1) {
+                    exp_step(16);
+                    exp_step(17);
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
         }
