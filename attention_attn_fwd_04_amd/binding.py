@@ -24,7 +24,7 @@ ATTN_ENOMEM = -4
 ATTN_ELAUNCH = -5
 ATTN_ENODEVICE = -6
 
-EXPORTED = ("attn_fwd", "attn_fwd_lse", "attn_decode", "attn_decode_workspace_bytes", "attn_bwd",
+EXPORTED = ("attn_fwd", "attn_fwd_lse", "attn_fwd_persistent", "attn_persistent_schedule", "attn_decode", "attn_decode_workspace_bytes", "attn_bwd",
             "attn_bwd_workspace_bytes", "attn_rope_apply", "attn_window_table", "attn_pruned_terms",
             "attn_check_args", "attn_strerror", "attn_release")
 
@@ -52,6 +52,10 @@ def lib():
     L.attn_fwd.restype = i
     L.attn_fwd_lse.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, f, i32p, vp]
     L.attn_fwd_lse.restype = i
+    L.attn_fwd_persistent.argtypes = [vp, vp, vp, vp, i, i, i, i, i, f, i, f, i32p, vp]
+    L.attn_fwd_persistent.restype = i
+    L.attn_persistent_schedule.argtypes = [i, i, i, i, ctypes.POINTER(ctypes.c_uint32), ctypes.c_longlong]
+    L.attn_persistent_schedule.restype = ctypes.c_longlong
     L.attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i, i, i, i, i, f, f, i32p, i, vp]
     L.attn_decode.restype = i
     L.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i, i]
@@ -109,6 +113,33 @@ def _check_tensor(t, name):
 def attn_fwd(q, k, v, o=None, *, rope_theta=10000.0, causal=True, scale=None,
              window_table=None, stream=None):
     """Fused causal attention forward with RoPE at load; returns o [B,S,Hq,D]."""
+    return _fwd("attn_fwd", q, k, v, o, rope_theta, causal, scale, window_table, stream)
+
+
+def attn_fwd_persistent(q, k, v, o=None, *, rope_theta=10000.0, causal=True, scale=None,
+                        window_table=None, stream=None):
+    """attn_fwd on the persistent, cost-balanced schedule of the causal query
+    tiles; returns o [B,S,Hq,D] (bitwise equal to attn_fwd's)."""
+    return _fwd("attn_fwd_persistent", q, k, v, o, rope_theta, causal, scale, window_table, stream)
+
+
+def attn_persistent_schedule(B, Hq, S, bins):
+    """The task list of attn_fwd_persistent for (B, Hq, S) over `bins` bins:
+    (offsets [bins'+1], tasks [n]) as numpy uint32 arrays, task =
+    qt | hq << 12 | b << 22."""
+    import numpy as np
+    n_tasks = B * Hq * ((S + 255) // 256)
+    cap = min(bins, n_tasks) + 1 + n_tasks
+    out = np.zeros(cap, dtype=np.uint32)
+    n = lib().attn_persistent_schedule(int(B), int(Hq), int(S), int(bins),
+                                       out.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32)), cap)
+    if n < 0:
+        raise AttnError(int(n), "attn_persistent_schedule")
+    nb = int(n) - 1 - n_tasks
+    return out[:nb + 1].copy(), out[nb + 1:int(n)].copy()
+
+
+def _fwd(entry, q, k, v, o, rope_theta, causal, scale, window_table, stream):
     import torch
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _check_tensor(t, n)
@@ -125,10 +156,10 @@ def attn_fwd(q, k, v, o=None, *, rope_theta=10000.0, causal=True, scale=None,
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     w, wp = _window_ptr(window_table, D)
-    st = lib().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), B, Hq, Hkv, S, D,
-                        float(rope_theta), int(bool(causal)), float(scale), wp, _stream_handle(stream))
+    st = getattr(lib(), entry)(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), B, Hq, Hkv, S, D,
+                               float(rope_theta), int(bool(causal)), float(scale), wp, _stream_handle(stream))
     if st != ATTN_OK:
-        raise AttnError(st, "attn_fwd")
+        raise AttnError(st, entry)
     return o
 
 

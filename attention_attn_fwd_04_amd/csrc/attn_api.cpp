@@ -152,6 +152,140 @@ int get_table(int dev, int D, float theta, int S, const uint16_t **out)
     return ATTN_OK;
 }
 
+// ---- persistent schedule ("Croqtile", "Step 4") ------------------------------
+// Task j = qt | hq << 12 | b << 22 for the 256-row query tile qt of head hq
+// of batch b.  The list holds bins + 1 bin offsets, then the tasks bin by bin.
+constexpr int kSchedTileRows = 256, kSchedKeyTile = 64;
+
+bool sched_fits(int B, int Hq, int S)
+{
+    return (S + kSchedTileRows - 1) / kSchedTileRows <= 4096 && Hq <= 1024 && B <= 1024;
+}
+
+// Cost of causal query tile qt: the 64-key tiles it visits plus 2 for its Q
+// load and epilogue (the pages' 2(bm + 1) + c, in this kernel's tile units).
+long long tile_cost(int qt, int S)
+{
+    const long long keys = std::min<long long>(S, (long long)(qt + 1) * kSchedTileRows);
+    return (keys + kSchedKeyTile - 1) / kSchedKeyTile + 2;
+}
+
+// Heads per band of the task list: about 64 query tiles per band (one head
+// at S = 16k, two at 8k, eight at 2k), as in attn_fwd's own work order.
+int sched_band_heads(int n_qt) { return std::max(1, 64 / n_qt); }
+
+// Bins are the work-groups of the launch; work-group g runs on XCD g % 8.
+// When the head count and the bin count are multiples of 8, XCD x takes the
+// heads [x n_bh / 8, (x + 1) n_bh / 8) (their K and V then stay in its L2);
+// otherwise one group spans all bins.  Within a group the heads go in bands;
+// band by band, the band's tasks go longest first to the bin with the least
+// work so far (lowest index on ties).  A bin runs its tasks in the order they
+// were dealt: band by band, so all bins of an XCD work on the same few heads
+// at a time, and within a band longest first.
+std::vector<uint32_t> build_schedule(int B, int Hq, int S, int bins)
+{
+    const int n_qt = (S + kSchedTileRows - 1) / kSchedTileRows;
+    const long long n_bh = (long long)B * Hq;
+    const long long n_tasks = n_bh * n_qt;
+    if (bins > n_tasks) bins = (int)n_tasks;
+    const int n_groups = (n_bh % 8 == 0 && bins % 8 == 0) ? 8 : 1;
+    const int kb = sched_band_heads(n_qt);
+    std::vector<std::vector<uint32_t>> bin_tasks(bins);
+    std::vector<long long> load(bins, 0);
+    for (int x = 0; x < n_groups; ++x) {
+        const long long h0 = x * n_bh / n_groups, h1 = (x + 1) * n_bh / n_groups;
+        for (long long hb = h0; hb < h1; hb += kb) {
+            std::vector<std::pair<long long, uint32_t>> ts;
+            for (long long bh = hb; bh < std::min(h1, hb + kb); ++bh) {
+                const uint32_t b = (uint32_t)(bh / Hq), hq = (uint32_t)(bh % Hq);
+                for (int qt = n_qt - 1; qt >= 0; --qt)
+                    ts.emplace_back(tile_cost(qt, S), (uint32_t)qt | hq << 12 | b << 22);
+            }
+            std::stable_sort(ts.begin(), ts.end(),
+                             [](const std::pair<long long, uint32_t> &u, const std::pair<long long, uint32_t> &v) {
+                                 return u.first > v.first;
+                             });
+            for (const auto &t : ts) {
+                int best = x;
+                for (int g = x; g < bins; g += n_groups)
+                    if (load[g] < load[best]) best = g;
+                bin_tasks[best].push_back(t.second);
+                load[best] += t.first;
+            }
+        }
+    }
+    std::vector<uint32_t> out;
+    out.reserve((size_t)bins + 1 + (size_t)n_tasks);
+    out.push_back(0);
+    for (int g = 0; g < bins; ++g) out.push_back(out.back() + (uint32_t)bin_tasks[g].size());
+    for (int g = 0; g < bins; ++g) out.insert(out.end(), bin_tasks[g].begin(), bin_tasks[g].end());
+    return out;
+}
+
+// Every index the kernel derives from the list stays in range: offsets rise
+// from 0 to the task count, and each (b, hq, qt) of the call is there once.
+bool check_schedule(const std::vector<uint32_t> &l, int B, int Hq, int S, int bins)
+{
+    const int n_qt = (S + kSchedTileRows - 1) / kSchedTileRows;
+    const long long n_tasks = (long long)B * Hq * n_qt;
+    if (bins < 1 || (long long)l.size() != bins + 1 + n_tasks || l[0] != 0 || (long long)l[bins] != n_tasks)
+        return false;
+    for (int g = 0; g < bins; ++g)
+        if (l[g + 1] < l[g]) return false;
+    std::vector<uint8_t> seen((size_t)n_tasks, 0);
+    for (long long j = 0; j < n_tasks; ++j) {
+        const uint32_t t = l[(size_t)(bins + 1 + j)];
+        const uint32_t qt = t & 4095u, hq = (t >> 12) & 1023u, b = t >> 22;
+        if ((int)qt >= n_qt || (int)hq >= Hq || (int)b >= B) return false;
+        uint8_t &f = seen[((size_t)b * Hq + hq) * n_qt + qt];
+        if (f) return false;
+        f = 1;
+    }
+    return true;
+}
+
+struct SchedKey {
+    int dev, B, Hq, S;
+    bool operator<(const SchedKey &o) const { return std::tie(dev, B, Hq, S) < std::tie(o.dev, o.B, o.Hq, o.S); }
+};
+struct SchedList {
+    const uint32_t *d = nullptr;
+    int bins = 0;
+};
+std::map<SchedKey, SchedList> g_sched;
+
+// The device copy of the task list for (dev, B, Hq, S) over one bin per
+// compute unit, built on first use.
+int get_schedule(int dev, int B, int Hq, int S, const uint32_t **out, int *bins_out)
+{
+    std::lock_guard<std::mutex> lk(g_mu);
+    SchedList &e = g_sched[SchedKey{dev, B, Hq, S}];
+    if (e.d == nullptr) {
+        int n_cu = 0;
+        if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu < 1) {
+            (void)hipGetLastError();
+            return ATTN_ENODEVICE;
+        }
+        const std::vector<uint32_t> l = build_schedule(B, Hq, S, n_cu);
+        const int bins = (int)(l.size() - 1 - (size_t)B * Hq * ((S + kSchedTileRows - 1) / kSchedTileRows));
+        if (!check_schedule(l, B, Hq, S, bins)) return ATTN_EINVAL;
+        void *dptr = nullptr;
+        if (hipMalloc(&dptr, l.size() * sizeof(uint32_t)) != hipSuccess) {
+            (void)hipGetLastError();
+            return ATTN_ENOMEM;
+        }
+        if (hipMemcpy(dptr, l.data(), l.size() * sizeof(uint32_t), hipMemcpyHostToDevice) != hipSuccess) {
+            (void)hipFree(dptr);
+            return ATTN_ELAUNCH;
+        }
+        e.d = static_cast<const uint32_t *>(dptr);
+        e.bins = bins;
+    }
+    *out = e.d;
+    *bins_out = e.bins;
+    return ATTN_OK;
+}
+
 int check_window(const int32_t *w, int D, int causal)
 {
     if (w == nullptr) return ATTN_OK;
@@ -163,10 +297,12 @@ int check_window(const int32_t *w, int D, int causal)
 }
 
 int fwd_common(const void *q, const void *k, const void *v, void *o, float *lse, int B, int Hq, int Hkv, int S,
-               int D, float rope_theta, int causal, float scale, const int32_t *window_table, void *stream)
+               int D, float rope_theta, int causal, float scale, const int32_t *window_table, void *stream,
+               bool persistent = false)
 {
     int st = attn_check_args(q, k, v, o, B, Hq, Hkv, S, D, rope_theta, causal, scale, window_table);
     if (st != ATTN_OK) return st;
+    if (persistent && (window_table != nullptr || !sched_fits(B, Hq, S))) return ATTN_EUNSUPPORTED;
     int dev = -1;
     st = current_device_ok(&dev);
     if (st != ATTN_OK) return st;
@@ -188,6 +324,10 @@ int fwd_common(const void *q, const void *k, const void *v, void *o, float *lse,
     }
     if (rope_theta != 0.0f) {
         st = get_table(dev, D, rope_theta, S, &a.rope_cs);
+        if (st != ATTN_OK) return st;
+    }
+    if (persistent && causal) {
+        st = get_schedule(dev, B, Hq, S, &a.sched, &a.sched_bins);
         if (st != ATTN_OK) return st;
     }
     if (attn::launch_attn_fwd(a, static_cast<hipStream_t>(stream)) != hipSuccess) return ATTN_ELAUNCH;
@@ -293,6 +433,24 @@ int attn_fwd_lse(const void *q, const void *k, const void *v, void *o, float *ls
         }
     }
     return fwd_common(q, k, v, o, lse, B, Hq, Hkv, S, D, rope_theta, causal, scale, window_table, stream);
+}
+
+int attn_fwd_persistent(const void *q, const void *k, const void *v, void *o, int B, int Hq, int Hkv, int S, int D,
+                        float rope_theta, int causal, float scale, const int32_t *window_table, void *stream)
+{
+    return fwd_common(q, k, v, o, nullptr, B, Hq, Hkv, S, D, rope_theta, causal, scale, window_table, stream, true);
+}
+
+long long attn_persistent_schedule(int B, int Hq, int S, int bins, uint32_t *out, long long cap)
+{
+    if (B < 1 || Hq < 1 || S < 1 || bins < 1 || out == nullptr) return ATTN_EINVAL;
+    if (!sched_fits(B, Hq, S)) return ATTN_EUNSUPPORTED;
+    const long long n_tasks = (long long)B * Hq * ((S + kSchedTileRows - 1) / kSchedTileRows);
+    const long long used = std::min<long long>(bins, n_tasks) + 1 + n_tasks;
+    if (cap < used) return ATTN_EINVAL;
+    const std::vector<uint32_t> l = build_schedule(B, Hq, S, bins);
+    std::memcpy(out, l.data(), l.size() * sizeof(uint32_t));
+    return (long long)l.size();
 }
 
 size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int L, int D, int num_splits)
@@ -526,8 +684,11 @@ void attn_release(void)
     for (auto &kv : g_tables)
         if (kv.second.cs) free_on(kv.first.dev, const_cast<uint16_t *>(kv.second.cs));
     for (auto &r : g_retired) free_on(r.first, r.second);
+    for (auto &kv : g_sched)
+        if (kv.second.d) free_on(kv.first.dev, const_cast<uint32_t *>(kv.second.d));
     g_tables.clear();
     g_retired.clear();
+    g_sched.clear();
     if (cur >= 0) (void)hipSetDevice(cur);
 }
 

@@ -34,6 +34,11 @@ struct FwdArgs {
     int use_window;
     float scale_log2e;  // scale * log2(e): scores enter exp2 directly
     int32_t window[kMaxPairs];
+    // Persistent schedule (null: one work-group per query tile): sched_bins + 1
+    // bin offsets, then the tasks qt | hq << 12 | b << 22, built and checked on
+    // the host; causal calls only.
+    const uint32_t *sched;
+    int sched_bins;
 };
 
 struct RopeArgs {

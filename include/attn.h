@@ -28,8 +28,8 @@
  *  - All arguments are validated on the host before anything is enqueued;
  *    on error nothing is launched and a negative attn_status is returned.
  *  - Calls on one device from several host threads are safe; the library's
- *    only shared state is its cache of RoPE cos/sin tables, guarded by a
- *    mutex.
+ *    only shared state is its cache of RoPE cos/sin tables and of persistent
+ *    task lists, guarded by a mutex.
  */
 #ifndef ATTN_MI355X_ATTN_H
 #define ATTN_MI355X_ATTN_H
@@ -91,13 +91,50 @@ int attn_fwd(const void *q, const void *k, const void *v, void *o,
  *  lse: fp32 device pointer to [B, Hq, S] (row-major, caller-owned, 4-byte
  *       aligned, not overlapping q, k, v or o); NULL is rejected unless B or
  *       S is 0.  All other arguments and errors are those of attn_fwd, and o
- *       is bitwise the same as attn_fwd's.  l is the sum of the
- *       bf16-rounded probabilities that also enter P V.
+ *       is bitwise the same as attn_fwd's.  l is the fp32 sum of the
+ *       probabilities (P V takes their bf16 roundings).
  */
 int attn_fwd_lse(const void *q, const void *k, const void *v, void *o, float *lse,
                  int B, int Hq, int Hkv, int S, int D,
                  float rope_theta, int causal, float scale,
                  const int32_t *window_table, void *stream);
+
+/*
+ * attn_fwd on a persistent, cost-balanced schedule of the causal query tiles
+ * ("Croqtile", "Step 4": persistent blocks fed from a task list built on the
+ * host, each task costed by its position on the diagonal, tasks dealt to the
+ * lightest bin, in an order that keeps K/V reuse).  One work-group per
+ * compute unit runs the 256-row query tiles of its bin one after another.  A
+ * tile's cost is the number of 64-key tiles it visits plus 2 (its Q load and
+ * epilogue).  When B*Hq and the bin count are multiples of 8, the heads are
+ * split evenly over the 8 XCDs (work-group g runs on XCD g % 8); otherwise
+ * one group spans all bins.  Within a group the heads go in bands of about
+ * 64 query tiles; band by band, tiles go longest first to the lightest bin,
+ * and each bin runs its tiles in that order.  The list for
+ * (device, B, Hq, S) is built and checked (every query tile exactly once) on
+ * the first call, copied to device memory and kept until attn_release.
+ *
+ *  Arguments, layout and errors as attn_fwd, and o is bitwise the same as
+ *  attn_fwd's.  causal == 0 runs attn_fwd's schedule (every tile then costs
+ *  the same).  ATTN_EUNSUPPORTED: a window_table, or S > 1048576, Hq > 1024
+ *  or B > 1024 (the task encoding).  ATTN_ENOMEM: the list's device copy
+ *  could not be allocated.
+ */
+int attn_fwd_persistent(const void *q, const void *k, const void *v, void *o,
+                        int B, int Hq, int Hkv, int S, int D,
+                        float rope_theta, int causal, float scale,
+                        const int32_t *window_table, void *stream);
+
+/*
+ * The task list attn_fwd_persistent uses for (B, Hq, S) over `bins` bins
+ * (min(bins, task count) are used), written to the HOST array out:
+ * out[0 .. bins'] the bin offsets, then the tasks qt | hq << 12 | b << 22 bin
+ * by bin, qt being the 256-row query tile.  Returns the number of uint32
+ * written, bins' + 1 + B*Hq*ceil(S/256); ATTN_EINVAL for a bad argument or
+ * cap below that, ATTN_EUNSUPPORTED beyond the limits of attn_fwd_persistent.
+ * Host only: no device is touched (for tests and inspection).
+ */
+long long attn_persistent_schedule(int B, int Hq, int S, int bins, uint32_t *out, long long cap);
 
 /*
  * Split-KV decode: one new query per sequence against its KV cache

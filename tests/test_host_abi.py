@@ -252,3 +252,92 @@ def test_bwd_empty_is_ok_without_device():
     z = dict(q=0, k=0, v=0, o=0, do=0, lse=0, dq=0, dk=0, dv=0, ws=0, nws=0)
     assert _bwd_call(B=0, **z) == binding.ATTN_OK
     assert _bwd_call(S=0, **z) == binding.ATTN_OK
+
+
+# ---- persistent schedule ("Croqtile", "Step 4": host task list, cost-balanced
+# bins, an order inside a bin that keeps K/V reuse) -----------------------------
+
+def _tile_cost(qt, S):
+    # the 64-key tiles a causal 256-row query tile visits, plus 2 for its Q
+    # load and epilogue
+    return -(-min(S, (qt + 1) * 256) // 64) + 2
+
+
+@pytest.mark.parametrize("B,Hq,S,bins", [
+    (4, 32, 8192, 256),     # prefill_s8192: 4096 tiles over 256 bins, 8 XCD groups
+    (1, 32, 16384, 256),    # gqa_s16384's 32 query heads: 2048 tiles
+    (1, 32, 32768, 256),    # window_s32768's shape
+    (1, 2, 256, 256),       # tiny: fewer tiles than bins -> one tile per bin
+    (2, 3, 1000, 256),      # 6 heads: one group over all bins, ragged S
+    (3, 8, 4000, 100),      # bin count not a multiple of 8: one group
+])
+def test_persistent_schedule_properties(B, Hq, S, bins):
+    off, tasks = binding.attn_persistent_schedule(B, Hq, S, bins)
+    n_qt = -(-S // 256)
+    n_tasks = B * Hq * n_qt
+    nb = min(bins, n_tasks)
+    # offsets: bins' + 1 entries rising from 0 to the task count
+    assert len(off) == nb + 1 and off[0] == 0 and off[-1] == n_tasks and len(tasks) == n_tasks
+    assert np.all(np.diff(off.astype(np.int64)) >= 0)
+    # every (b, hq, qt) exactly once
+    qt, hq, b = tasks & 4095, (tasks >> 12) & 1023, tasks >> 22
+    assert qt.max() < n_qt and hq.max() < Hq and b.max() < B
+    flat = (b.astype(np.int64) * Hq + hq) * n_qt + qt
+    assert np.array_equal(np.sort(flat), np.arange(n_tasks))
+    cost = np.array([_tile_cost(int(t), S) for t in qt])
+    n_bh = B * Hq
+    groups = 8 if (n_bh % 8 == 0 and nb % 8 == 0) else 1
+    loads = np.array([cost[off[g]:off[g + 1]].sum() for g in range(nb)])
+    for x in range(groups):
+        gb = list(range(x, nb, groups))
+        # XCD grouping: bin g holds only the heads of group g % 8
+        if groups == 8:
+            h0, h1 = x * n_bh // 8, (x + 1) * n_bh // 8
+            for g in gb:
+                bh = b[off[g]:off[g + 1]].astype(np.int64) * Hq + hq[off[g]:off[g + 1]]
+                assert np.all((bh >= h0) & (bh < h1))
+        # longest-first to the lightest bin: no bin exceeds the lightest by
+        # more than the largest task of the group
+        gl = loads[gb]
+        assert gl.max() - gl.min() <= max(cost[off[g]:off[g + 1]].max(initial=0) for g in gb)
+    # inside a bin: band by band (bands of max(1, 64 // n_qt) heads), longest
+    # tile first within a band
+    kb = max(1, 64 // n_qt)
+    band = (b.astype(np.int64) * Hq + hq) // kb
+    for g in range(nb):
+        key = list(zip(band[off[g]:off[g + 1]].tolist(), (-cost[off[g]:off[g + 1]]).tolist()))
+        assert key == sorted(key)
+
+
+def test_persistent_schedule_balance_prefill_s8192():
+    """The 4096 query tiles of B4 H32 S8192 over 256 bins: every bin within
+    one tile's cost of the mean (the causal costs run 6..130)."""
+    off, tasks = binding.attn_persistent_schedule(4, 32, 8192, 256)
+    cost = np.array([_tile_cost(int(t) & 4095, 8192) for t in tasks])
+    loads = np.array([cost[off[g]:off[g + 1]].sum() for g in range(256)])
+    assert loads.sum() == cost.sum()
+    assert loads.max() - loads.min() <= 130
+    assert loads.max() <= loads.mean() * 1.05
+
+
+def test_persistent_schedule_argument_errors():
+    for args in ((0, 32, 8192, 256), (4, 0, 8192, 256), (4, 32, 0, 256), (4, 32, 8192, 0)):
+        with pytest.raises(binding.AttnError):
+            binding.attn_persistent_schedule(*args)
+    with pytest.raises(binding.AttnError) as e:
+        binding.attn_persistent_schedule(1, 2000, 256, 256)     # hq does not fit 10 bits
+    assert e.value.status == binding.ATTN_EUNSUPPORTED
+    out = np.zeros(4, dtype=np.uint32)
+    n = binding.lib().attn_persistent_schedule(1, 2, 256, 256, out.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32)), 4)
+    assert n == binding.ATTN_EINVAL   # needs 3 offsets + 2 tasks = 5
+
+
+def test_fwd_persistent_rejects_window():
+    """attn_fwd_persistent with fake device addresses: the window and size
+    limits are argument errors caught before any device call."""
+    w = (ctypes.c_int32 * 64)(*([1 << 20] * 64))
+    call = binding.lib().attn_fwd_persistent
+    assert call(A, A * 64, A * 128, A * 192, 1, 4, 2, 128, 128, 1e4, 1, 0.088, w, None) == binding.ATTN_EUNSUPPORTED
+    assert call(A, A * 64, A * 128, A * 192, 1, 2048, 2048, 1, 128, 1e4, 1, 0.088, None, None) == \
+        binding.ATTN_EUNSUPPORTED
+    assert call(A, A * 64, A * 128, A * 192, 1, 4, 3, 128, 128, 1e4, 1, 0.088, None, None) == binding.ATTN_EINVAL
