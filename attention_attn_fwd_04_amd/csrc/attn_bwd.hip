@@ -379,7 +379,17 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(const BwdArgs a)
         }
         interleave_reads_mfma<2 * G::KCH, 1>();
         __builtin_amdgcn_sched_barrier(0);
-        // dS^T = P^T o (dP^T - Delta) with masked P set to zero
+        // dS^T = P^T o (dP^T - Delta) with masked P set to zero: on the key
+        // tiles that cross this wave's first query or the end of the sequence
+        // (a wave-uniform test) the masked scores become -inf, so their P is
+        // exp2(-inf) = 0; the other tiles keep every entry.
+        if ((CAUSAL && m0 + kBwdBN - 1 > nw0) || m0 + kBwdBN > S) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int m = m0 + 8 * (i >> 2) + 4 * g + (i & 3);
+                s[i] = ((CAUSAL && m > n) || m >= S) ? -__builtin_inff() : s[i];
+            }
+        }
         bf16x8_t dsop[2];
 #pragma unroll
         for (int ch = 0; ch < 2; ++ch) {
@@ -390,9 +400,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(const BwdArgs a)
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int i = 8 * ch + 2 * e + h;
-                    const int m = m0 + 8 * (i >> 2) + 4 * g + (i & 3);
-                    const bool keep = !((CAUSAL && m > n) || m >= S);
-                    const float p = keep ? fast_exp2(s[i]) : 0.f;
+                    const float p = fast_exp2(s[i]);
                     v2[h] = p * (dp[i] - dlt);
                 }
                 w4[e] = pack_bf16x2(v2[0], v2[1]);
@@ -534,7 +542,17 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
         }
         interleave_reads_mfma<2 * G::KCH, 1>();
         __builtin_amdgcn_sched_barrier(0);
-        // P and dS = P o (dP - Delta), masked entries zero
+        // P and dS = P o (dP - Delta), masked entries zero: on the query
+        // tiles that cross this wave's last key or the end of the sequence (a
+        // wave-uniform test) the masked scores become -inf, so their P is
+        // exp2(-inf) = 0; the other tiles keep every entry.
+        if ((CAUSAL && n0 < mw0 + 31) || n0 + kBwdBN > S || mw0 + 32 > S) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int nq = n0 + 8 * (i >> 2) + 4 * g + (i & 3);
+                s[i] = ((CAUSAL && nq < m) || nq >= S || m >= S) ? -__builtin_inff() : s[i];
+            }
+        }
         bf16x8_t pop[2], dsop[2];
 #pragma unroll
         for (int ch = 0; ch < 2; ++ch) {
@@ -548,9 +566,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int j = 2 * e + h, i = 8 * ch + j;
-                    const int nq = n0 + 8 * (i >> 2) + 4 * g + (i & 3);
-                    const bool keep = !((CAUSAL && nq < m) || nq >= S || m >= S);
-                    const float p = keep ? fast_exp2(s[i]) : 0.f;
+                    const float p = fast_exp2(s[i]);
                     pv[h] = p;
                     dsv[h] = p * (dp[i] - dl[j]);
                 }
