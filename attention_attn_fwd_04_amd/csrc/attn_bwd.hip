@@ -102,20 +102,28 @@ struct TileReader {
     int lane_;
     __device__ __forceinline__ void init(int lane) { lane_ = lane; }
     __device__ __forceinline__ void refresh() { asm volatile("" : "+v"(lane_)); }
+    // Chunk kc + PG g of row l32 sits at l32 ROWB + ((kc + PG g) ^ kx(l32)) 16.
+    // kc and PG g occupy disjoint bits, so that is the lane's chunk-0 address
+    // XOR kc 16: one XOR per read once the lane part is known (tile bases are
+    // multiples of 256 bytes, so the XOR never reaches them).
     __device__ __forceinline__ bf16x8_t row(uint32_t base, int kc) const
     {
         const int l32 = lane_ & 31, g = lane_ >> 5;
-        return *(const lds_bf16x8_t *)lds_ptr(base + (uint32_t)G::off(l32, kc + G::PG * g));
+        const uint32_t lane_off = (uint32_t)(l32 * G::ROWB + (((G::PG * g) ^ G::kx(l32)) << 4));
+        return *(const lds_bf16x8_t *)lds_ptr((base + lane_off) ^ (uint32_t)(kc << 4));
     }
-    // rows 16 ch + ...: the chunk permutation repeats every 16 rows
+    // rows 16 ch + ...: the chunk permutation repeats every 16 rows.  Chunk
+    // 4 db + c0 (c0 < 4) XOR kx(r) = (c0 XOR kx(r)) XOR 4 db: the lane's db = 0
+    // address XOR db 64.
     __device__ __forceinline__ bf16x8_t tr(uint32_t base, int ch, int db) const
     {
         const int g = lane_ >> 5;
         const int tr_row = (lane_ & 15) >> 2;
         const int tr_dim = 16 * ((lane_ >> 4) & 1) + 4 * (lane_ & 3);
-        const lds_u8_t *p0 = lds_ptr(base + (uint32_t)G::dim_off(4 * g + tr_row, 32 * db + tr_dim)) + 16 * ch * G::ROWB;
-        const lds_u8_t *p1 =
-            lds_ptr(base + (uint32_t)G::dim_off(4 * g + tr_row + 8, 32 * db + tr_dim)) + 16 * ch * G::ROWB;
+        const uint32_t a0 = (base + (uint32_t)G::dim_off(4 * g + tr_row, tr_dim)) ^ (uint32_t)(db << 6);
+        const uint32_t a1 = (base + (uint32_t)G::dim_off(4 * g + tr_row + 8, tr_dim)) ^ (uint32_t)(db << 6);
+        const lds_u8_t *p0 = lds_ptr(a0) + 16 * ch * G::ROWB;
+        const lds_u8_t *p1 = lds_ptr(a1) + 16 * ch * G::ROWB;
         const i16x4_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)p0);
         const i16x4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)p1);
         const uint2 u0 = __builtin_bit_cast(uint2, t0), u1 = __builtin_bit_cast(uint2, t1);
@@ -428,7 +436,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
 {
     using G = BGeo<D>;
     __shared__ __attribute__((aligned(16))) uint8_t smem[4 * G::TILE_B];   // Q and dO, two slots each
-    __shared__ __attribute__((aligned(16))) float rowv[2][2][kBwdBN];      // L log2 e and Delta, two slots
+    __shared__ __attribute__((aligned(16))) float rowv[2][2][kBwdBN];      // -L log2 e and Delta, two slots
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l32 = lane & 31, g = lane >> 5;
@@ -476,7 +484,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
         if (wave == 0 && lane < kBwdBN) {
             const int hq = hq0 + u / nt, nq = (t0 + u % nt) * kBwdBN + lane;
             const size_t rowid = ((size_t)b * a.Hq + hq) * S + nq;
-            pre_l = nq < S ? a.lse[rowid] * kLog2e : 0.f;
+            pre_l = nq < S ? -(a.lse[rowid] * kLog2e) : 0.f;   // the start of the S chain
             pre_d = nq < S ? a.delta[rowid] : 0.f;
         }
     };
@@ -527,10 +535,10 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
             const float4 l4 = *reinterpret_cast<const float4 *>(lrow + 8 * q4 + 4 * g);
-            s[4 * q4 + 0] = -l4.x;
-            s[4 * q4 + 1] = -l4.y;
-            s[4 * q4 + 2] = -l4.z;
-            s[4 * q4 + 3] = -l4.w;
+            s[4 * q4 + 0] = l4.x;
+            s[4 * q4 + 1] = l4.y;
+            s[4 * q4 + 2] = l4.z;
+            s[4 * q4 + 3] = l4.w;
         }
 #pragma unroll
         for (int i = 0; i < 16; ++i) dp[i] = 0.f;
