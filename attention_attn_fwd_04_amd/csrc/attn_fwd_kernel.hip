@@ -57,6 +57,10 @@
 //    ones.  Query tiles are issued longest first within bands of heads, and
 //    the block index is remapped so a band's tiles run on one XCD (shared
 //    L2 for its K/V).
+//  * The same per-tile code also runs persistently ("Flash Attention: Causal
+//    Prefill D=128", "Step 4"): one work-group per compute unit walks the
+//    query tiles of its bin in a task list that the host built (cost-balanced
+//    bins, heads grouped per XCD) and checked.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
