@@ -3,8 +3,8 @@
 The LSE of a row is a softmax-weighted mean of its scores plus log l, so its
 error is that of the scores (the kernel rounds Q' and K' to bf16: a relative
 2^-9 per element, about 4e-3 per scaled score for N(0,1) inputs at D = 128)
-plus the relative error of l (a sum of bf16-rounded probabilities, at most
-2^-9).  The same bar as the outputs therefore applies: max |err| <= 2e-2 and
+plus the relative error of l (an fp32 sum of probabilities computed from
+those scores; the fp32 rounding of the sum adds well under 2^-9).  The same bar as the outputs therefore applies: max |err| <= 2e-2 and
 mean |err| <= 2e-3.  o must be bitwise the output of attn_fwd.
 """
 import math
