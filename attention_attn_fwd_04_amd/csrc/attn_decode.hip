@@ -228,20 +228,24 @@ __global__ __launch_bounds__(kDecWaves * 64, 1) void decode_split_kernel(const D
         const float alpha = (m_new == m_run) ? 1.0f : fast_exp2((m_run - m_new) * c);
         m_run = m_new;
         const float nmc = -m_new * c;
+        // P in bf16 for the PV MFMAs; the row sum adds the fp32 P (two
+        // independent chains) as the prefill kernel does.
         bf16x8_t pf[2];
-        float rs = 0.f;
+        float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
         for (int ch = 0; ch < 2; ++ch) {
             uint32_t w4[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                w4[e] = pack_bf16x2(fast_exp2(__builtin_fmaf(s[8 * ch + 2 * e], c, nmc)),
-                                    fast_exp2(__builtin_fmaf(s[8 * ch + 2 * e + 1], c, nmc)));
-                rs = sum_bf16x2(w4[e], rs);
+                const float p0 = fast_exp2(__builtin_fmaf(s[8 * ch + 2 * e], c, nmc));
+                const float p1 = fast_exp2(__builtin_fmaf(s[8 * ch + 2 * e + 1], c, nmc));
+                w4[e] = pack_bf16x2(p0, p1);
+                rs0 += p0;
+                rs1 += p1;
             }
             pf[ch] = __builtin_bit_cast(bf16x8_t, make_uint4(w4[0], w4[1], w4[2], w4[3]));
         }
-        l_run = l_run * alpha + rs;
+        l_run = l_run * alpha + (rs0 + rs1);
 
         // O^T = alpha O^T + V^T P^T.
         const uint32_t vbase = lds_addr(vslot(t));
