@@ -100,14 +100,38 @@ def _stream_handle(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _check_tensor(t, name):
+def _check_tensor(t, name, like=None):
     import torch
     if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or t.dim() != 4:
         raise TypeError("%s must be a 4-d bfloat16 tensor [B, S, H, D]" % name)
-    if not t.is_cuda:
-        raise TypeError("%s must be a device tensor" % name)
+    _check_device(t, name, like)
     if not t.is_contiguous():
         raise ValueError("%s must be contiguous (BSHD)" % name)
+
+
+def _check_device(t, name, like=None):
+    """Every tensor whose address reaches the library must live on the GPU,
+    on the device of the call's first input (a host address handed to a
+    kernel faults the GPU)."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch tensor" % name)
+    if not t.is_cuda:
+        raise TypeError("%s must be a device tensor" % name)
+    if like is not None and t.device != like.device:
+        raise ValueError("%s must be on %s like the inputs (got %s)" % (name, like.device, t.device))
+
+
+def _check_buffer(t, name, like, dtype, shape=None):
+    """A device buffer the library reads or writes: dtype, device, shape and
+    contiguity checked before anything is enqueued."""
+    _check_device(t, name, like)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s" % (name, dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s (got %s)" % (name, tuple(shape), tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
 
 
 def attn_fwd(q, k, v, o=None, *, rope_theta=10000.0, causal=True, scale=None,
@@ -142,7 +166,7 @@ def attn_persistent_schedule(B, Hq, S, bins):
 def _fwd(entry, q, k, v, o, rope_theta, causal, scale, window_table, stream):
     import torch
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _check_tensor(t, n)
+        _check_tensor(t, n, q)
     B, S, Hq, D = q.shape
     Hkv = k.shape[2]
     if k.shape != (B, S, Hkv, D) or v.shape != k.shape:
@@ -150,7 +174,7 @@ def _fwd(entry, q, k, v, o, rope_theta, causal, scale, window_table, stream):
     if o is None:
         o = torch.empty_like(q)
     else:
-        _check_tensor(o, "o")
+        _check_tensor(o, "o", q)
         if o.shape != q.shape:
             raise ValueError("o must have q's shape")
     if scale is None:
@@ -169,7 +193,7 @@ def attn_fwd_lse(q, k, v, o=None, lse=None, *, rope_theta=10000.0, causal=True, 
     (o [B,S,Hq,D] bf16, lse [B,Hq,S] fp32)."""
     import torch
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _check_tensor(t, n)
+        _check_tensor(t, n, q)
     B, S, Hq, D = q.shape
     Hkv = k.shape[2]
     if k.shape != (B, S, Hkv, D) or v.shape != k.shape:
@@ -177,14 +201,13 @@ def attn_fwd_lse(q, k, v, o=None, lse=None, *, rope_theta=10000.0, causal=True, 
     if o is None:
         o = torch.empty_like(q)
     else:
-        _check_tensor(o, "o")
+        _check_tensor(o, "o", q)
         if o.shape != q.shape:
             raise ValueError("o must have q's shape")
     if lse is None:
         lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
-    elif (not isinstance(lse, torch.Tensor) or lse.dtype != torch.float32 or not lse.is_cuda
-          or tuple(lse.shape) != (B, Hq, S) or not lse.is_contiguous()):
-        raise ValueError("lse must be a contiguous float32 device tensor [B, Hq, S]")
+    else:
+        _check_buffer(lse, "lse", q, torch.float32, (B, Hq, S))
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     w, wp = _window_ptr(window_table, D)
@@ -207,25 +230,30 @@ def attn_decode(q, k, v, o=None, lse=None, workspace=None, *, rope_theta=10000.0
     want_lse or an lse buffer is given)."""
     import torch
     for t, n in ((k, "k"), (v, "v")):
-        _check_tensor(t, n)
+        _check_tensor(t, n, k)
     B, L, Hkv, D = k.shape
     if v.shape != k.shape:
         raise ValueError("v must match k [B, L, Hkv, D]")
-    if (not isinstance(q, torch.Tensor) or q.dtype != torch.bfloat16 or q.dim() != 3 or not q.is_cuda
-            or not q.is_contiguous() or q.shape[0] != B or q.shape[2] != D):
-        raise ValueError("q must be a contiguous bfloat16 device tensor [B, Hq, D]")
+    if (not isinstance(q, torch.Tensor) or q.dtype != torch.bfloat16 or q.dim() != 3
+            or q.shape[0] != B or q.shape[2] != D):
+        raise ValueError("q must be a bfloat16 tensor [B, Hq, D]")
+    _check_buffer(q, "q", k, torch.bfloat16)
     Hq = q.shape[1]
     if o is None:
         o = torch.empty_like(q)
-    elif o.shape != q.shape or o.dtype != torch.bfloat16 or not o.is_contiguous():
-        raise ValueError("o must be a contiguous bfloat16 tensor shaped like q")
+    else:
+        _check_buffer(o, "o", k, torch.bfloat16, q.shape)
     if lse is None and want_lse:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq) or not lse.is_contiguous()):
-        raise ValueError("lse must be a contiguous float32 tensor [B, Hq]")
+    if lse is not None:
+        _check_buffer(lse, "lse", k, torch.float32, (B, Hq))
     nbytes = attn_decode_workspace_bytes(B, Hq, Hkv, L, D, num_splits)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    else:
+        _check_device(workspace, "workspace", k)
+        if not workspace.is_contiguous():
+            raise ValueError("workspace must be contiguous")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     w, wp = _window_ptr(window_table, D)
@@ -249,26 +277,28 @@ def attn_bwd(q, k, v, o, lse, dout, dq=None, dk=None, dv=None, workspace=None, *
     (attn_fwd_lse with the same arguments) and the output gradient dout."""
     import torch
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
-        _check_tensor(t, n)
+        _check_tensor(t, n, q)
     B, S, Hq, D = q.shape
     Hkv = k.shape[2]
     if k.shape != (B, S, Hkv, D) or v.shape != k.shape:
         raise ValueError("k and v must be [B, S, Hkv, D] matching q")
     if o.shape != q.shape or dout.shape != q.shape:
         raise ValueError("o and dout must be shaped like q")
-    if (not isinstance(lse, torch.Tensor) or lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, S)
-            or not lse.is_contiguous()):
-        raise ValueError("lse must be a contiguous float32 tensor [B, Hq, S]")
+    _check_buffer(lse, "lse", q, torch.float32, (B, Hq, S))
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     for t, n, ref in ((dq, "dq", q), (dk, "dk", k), (dv, "dv", v)):
-        _check_tensor(t, n)
+        _check_tensor(t, n, q)
         if t.shape != ref.shape:
             raise ValueError("%s must be shaped like %s" % (n, "q" if ref is q else "k"))
     nbytes = attn_bwd_workspace_bytes(B, Hq, Hkv, S, D)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    else:
+        _check_device(workspace, "workspace", q)
+        if not workspace.is_contiguous():
+            raise ValueError("workspace must be contiguous")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     w, wp = _window_ptr(window_table, D)
@@ -284,16 +314,18 @@ def attn_bwd(q, k, v, o, lse, dout, dq=None, dk=None, dv=None, workspace=None, *
 def attn_rope_apply(q, k, q_out=None, k_out=None, *, rope_theta=10000.0, stream=None):
     """Separate RoPE pass: rotated copies (q_out, k_out) of q and k."""
     import torch
-    _check_tensor(q, "q")
-    _check_tensor(k, "k")
+    _check_tensor(q, "q", q)
+    _check_tensor(k, "k", q)
     B, S, Hq, D = q.shape
     Hkv = k.shape[2]
     if k.shape != (B, S, Hkv, D):
         raise ValueError("k must be [B, S, Hkv, D] matching q")
     q_out = torch.empty_like(q) if q_out is None else q_out
     k_out = torch.empty_like(k) if k_out is None else k_out
-    _check_tensor(q_out, "q_out")
-    _check_tensor(k_out, "k_out")
+    _check_tensor(q_out, "q_out", q)
+    _check_tensor(k_out, "k_out", q)
+    if q_out.shape != q.shape or k_out.shape != k.shape:
+        raise ValueError("q_out and k_out must be shaped like q and k")
     st = lib().attn_rope_apply(q.data_ptr(), k.data_ptr(), q_out.data_ptr(), k_out.data_ptr(),
                                B, Hq, Hkv, S, D, float(rope_theta), _stream_handle(stream))
     if st != ATTN_OK:

@@ -71,7 +71,10 @@ __device__ __forceinline__ T &lds_at(uint8_t *base, int off) { return *reinterpr
 // write zeros.  Issued through inline assembly so that the compiler does not
 // treat these asynchronous LDS writes as pending on every later LDS read and
 // barrier; the kernel waits for them itself (wait_vmcnt) before the barrier
-// that publishes the tile.  One wait state separates the M0 write from its use.
+// that publishes the tile.  M0 is an input operand of the statement (the
+// "{m0}" constraint): the compiler writes it and knows it is in use.  It
+// cannot see that the statement reads M0 as the LDS base, so the statement
+// starts with the one wait state an LDS DMA needs after an SALU write of M0.
 // The same kind of buffer resource as four 32-bit words (base, stride 0,
 // size, flags), for the inline assembly below, which takes it as a scalar
 // operand.
@@ -99,10 +102,10 @@ __device__ __forceinline__ void dma16(u32x4_t r, uint32_t voff, const uint8_t *l
     rs.y = __builtin_amdgcn_readfirstlane(r.y);
     rs.z = __builtin_amdgcn_readfirstlane(r.z);
     rs.w = __builtin_amdgcn_readfirstlane(r.w);
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                  :
-                 : "v"(voff), "s"(rs), "s"(m0)
-                 : "memory", "m0");
+                 : "v"(voff), "s"(rs), "{m0}"(m0)
+                 : "memory");
 }
 
 // The same with the LDS destination as a 32-bit LDS byte address (no
@@ -115,10 +118,10 @@ __device__ __forceinline__ void dma16(u32x4_t r, uint32_t voff, uint32_t lds_bas
     rs.y = __builtin_amdgcn_readfirstlane(r.y);
     rs.z = __builtin_amdgcn_readfirstlane(r.z);
     rs.w = __builtin_amdgcn_readfirstlane(r.w);
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                  :
-                 : "v"(voff), "s"(rs), "s"(m0)
-                 : "memory", "m0");
+                 : "v"(voff), "s"(rs), "{m0}"(m0)
+                 : "memory");
 }
 
 // s_waitcnt on the vector-memory counter only: at most n loads of this wave

@@ -3,15 +3,10 @@
 The forward output o and its lse come from attn_fwd_lse on the GPU, as in
 training; the oracle recomputes everything from q, k, v and dout in fp64.
 
-Tolerance.  The pages verify gradients against a plain reference with FA2's
-fp16 bar, |err| < 2e-2 ("AttnFuse", section 6.6 "Correctness").  The
-gradients here are stored in bf16, whose rounding alone is up to 2^-9 |g|
-and exceeds 2e-2 once |g| > 10 (dq and dk of rows with peaked softmax reach
-that), so the element bar is 2e-2 + 2^-8 |ref| (the absolute bar plus one
-bf16 ulp of the stored value).  The mean bar is the forward's 2e-3 plus the
-same relative term over the tensor, 2e-3 + 2^-8 mean|ref|: the dominant
-error, Delta = rowsum(dO o O) taken from the bf16 forward output and dS
-rounded to bf16, grows with |dP| = |<dO, V>|, i.e. with the gradients.
+Tolerance: tests/grad_bars.py (2e-2 + 2^-8 |ref| per element, 2e-3 +
+2^-8 mean|ref| for a tensor's mean error), derived there from the kernels'
+bf16 rounding chain; tests/test_bwd_bar_controls.py shows on the CPU that an
+emulation of that chain passes it and that plausible slips fail it.
 """
 import math
 
@@ -21,11 +16,10 @@ import torch
 
 from attention_attn_fwd_04_amd import binding
 from attention_attn_fwd_04_amd.inputs import CONFIGS, CONFIG_SEEDS, bf16_bits, make_qkv
+from grad_bars import ABS_TOL, MEAN_ABS_TOL, MEAN_REL_TOL, REL_TOL, grad_bar
 from oracle import oracle as O
 
 pytestmark = pytest.mark.gpu
-
-ABS_TOL, REL_TOL, MEAN_TOL = 2e-2, 2.0 ** -8, 2e-3
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -51,15 +45,10 @@ def _run(q, k, v, do, theta, causal, scale):
 
 def _check(got, ref, label):
     for name, g, r in zip(("dq", "dk", "dv"), got, ref):
-        err = np.abs(g - r)
-        bar = ABS_TOL + REL_TOL * np.abs(r)
-        worst = np.unravel_index(np.argmax(err - bar), err.shape)
-        print("%s %s max_abs=%.3e mean_abs=%.3e max|ref|=%.3e worst=%s (err %.3e ref %.3e)"
-              % (label, name, err.max(), err.mean(), np.abs(r).max(), worst, err[worst], r[worst]), flush=True)
-        assert np.isfinite(g).all(), (label, name)
-        assert (err <= bar).all(), (label, name, worst)
-        if err.size >= 32:
-            assert err.mean() <= MEAN_TOL + REL_TOL * np.abs(r).mean(), (label, name, err.mean())
+        ok, d = grad_bar(g, r)
+        print("%s %s max_abs=%.3e mean_abs=%.3e (mean bar %.3e) max|ref|=%.3e worst=%s"
+              % (label, name, d["max_abs"], d["mean_abs"], d["mean_bar"], np.abs(r).max(), d["worst"]), flush=True)
+        assert ok, (label, name, d)
 
 
 CASES = [
@@ -110,7 +99,7 @@ def test_bwd_zero_queries_closed_form():
     err = np.abs(dv - ref)
     print("zero-q dv max_abs=%.3e mean_abs=%.3e" % (err.max(), err.mean()), flush=True)
     assert (err <= ABS_TOL + REL_TOL * np.abs(ref)).all()
-    assert err.mean() <= MEAN_TOL + REL_TOL * np.abs(ref).mean()
+    assert err.mean() <= MEAN_ABS_TOL + MEAN_REL_TOL * np.abs(ref).mean()
     assert not dk.any()
     assert np.isfinite(dq).all()
 

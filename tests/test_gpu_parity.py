@@ -232,3 +232,21 @@ def test_full_size_config_sampled(name):
     ref = O.attn_rows(bf16_bits(q), bf16_bits(k), bf16_bits(v), rows, theta, True, scale, w)
     assert_parity(o, ref, rows=rows, label=name)
     assert torch.isfinite(o.float()).all()
+
+
+@pytest.mark.parametrize("name", ["prefill_s4096", "prefill_s8192"])
+def test_separate_path_full_size_sampled(name):
+    """The separate variant the crossover measures ("AttnFuse", section 5.3):
+    attn_rope_apply into a workspace, then attn_fwd with RoPE off, at the full
+    configurations in the benchmark's launch configuration, on sampled rows
+    against the oracle with RoPE on."""
+    cfg = CONFIGS[name]
+    B, Hq, Hkv, S, D, theta = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["S"], cfg["D"], cfg["theta"]
+    print("separate full size %s" % name, flush=True)
+    q, k, v = make_qkv(B, S, Hq, Hkv, D, seed=CONFIG_SEEDS[name])
+    scale = 1 / math.sqrt(D)
+    o = run_separate(q, k, v, theta, True, scale)
+    rows = sample_rows(B, S, Hq, n_heads=6, seed=CONFIG_SEEDS[name] + 1)
+    ref = O.attn_rows(bf16_bits(q), bf16_bits(k), bf16_bits(v), rows, theta, True, scale, None)
+    assert_parity(o, ref, rows=rows, label="separate " + name)
+    assert torch.isfinite(o.float()).all()

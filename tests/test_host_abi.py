@@ -341,3 +341,22 @@ def test_fwd_persistent_rejects_window():
     assert call(A, A * 64, A * 128, A * 192, 1, 2048, 2048, 1, 128, 1e4, 1, 0.088, None, None) == \
         binding.ATTN_EUNSUPPORTED
     assert call(A, A * 64, A * 128, A * 192, 1, 4, 3, 128, 128, 1e4, 1, 0.088, None, None) == binding.ATTN_EINVAL
+
+
+def test_binding_rejects_host_tensors_before_any_call():
+    """A host tensor's address handed to a kernel would fault the GPU: every
+    wrapper rejects host tensors before it reaches the library."""
+    import torch
+    q = torch.zeros(1, 64, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        binding.attn_fwd(q, q, q)
+    with pytest.raises(TypeError):
+        binding.attn_fwd_lse(q, q, q)
+    with pytest.raises(TypeError):
+        binding.attn_fwd_persistent(q, q, q)
+    with pytest.raises(TypeError):
+        binding.attn_rope_apply(q, q)
+    with pytest.raises(TypeError):
+        binding.attn_decode(q[:, 0].contiguous(), q, q)
+    with pytest.raises(TypeError):
+        binding.attn_bwd(q, q, q, q, torch.zeros(1, 2, 64), q)
