@@ -72,9 +72,13 @@ __device__ __forceinline__ T &lds_at(uint8_t *base, int off) { return *reinterpr
 // treat these asynchronous LDS writes as pending on every later LDS read and
 // barrier; the kernel waits for them itself (wait_vmcnt) before the barrier
 // that publishes the tile.  M0 is an input operand of the statement (the
-// "{m0}" constraint): the compiler writes it and knows it is in use.  It
-// cannot see that the statement reads M0 as the LDS base, so the statement
-// starts with the one wait state an LDS DMA needs after an SALU write of M0.
+// "{m0}" constraint): the compiler writes it and knows it is in use.
+// The compiler checks no hazards on the scalar operands of an inline
+// statement, so the statement starts with five wait states itself: a VALU
+// write of an SGPR (the descriptor words often come from v_readfirstlane)
+// needs 5 before a VMEM instruction reads it, an SALU write of M0 needs 1
+// before an LDS DMA.  With fewer, a load can take a descriptor word's
+// previous value, another buffer's base address, and read out of bounds.
 // The same kind of buffer resource as four 32-bit words (base, stride 0,
 // size, flags), for the inline assembly below, which takes it as a scalar
 // operand.
@@ -102,7 +106,7 @@ __device__ __forceinline__ void dma16(u32x4_t r, uint32_t voff, const uint8_t *l
     rs.y = __builtin_amdgcn_readfirstlane(r.y);
     rs.z = __builtin_amdgcn_readfirstlane(r.z);
     rs.w = __builtin_amdgcn_readfirstlane(r.w);
-    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                  :
                  : "v"(voff), "s"(rs), "{m0}"(m0)
                  : "memory");
@@ -118,7 +122,7 @@ __device__ __forceinline__ void dma16(u32x4_t r, uint32_t voff, uint32_t lds_bas
     rs.y = __builtin_amdgcn_readfirstlane(r.y);
     rs.z = __builtin_amdgcn_readfirstlane(r.z);
     rs.w = __builtin_amdgcn_readfirstlane(r.w);
-    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                  :
                  : "v"(voff), "s"(rs), "{m0}"(m0)
                  : "memory");
