@@ -23,8 +23,10 @@ ATTN_EALIGN = -3
 ATTN_ENOMEM = -4
 ATTN_ELAUNCH = -5
 ATTN_ENODEVICE = -6
+ATTN_ESCRATCH = -7
 
-EXPORTED = ("attn_fwd", "attn_fwd_lse", "attn_fwd_persistent", "attn_persistent_schedule", "attn_decode", "attn_decode_workspace_bytes", "attn_bwd",
+EXPORTED = ("attn_fwd", "attn_fwd_lse", "attn_fwd_persistent", "attn_persistent_schedule", "attn_decode",
+            "attn_decode_workspace_bytes", "attn_decode_noalloc", "attn_decode_scratch_bytes", "attn_bwd",
             "attn_bwd_workspace_bytes", "attn_rope_apply", "attn_window_table", "attn_pruned_terms",
             "attn_check_args", "attn_strerror", "attn_release")
 
@@ -60,6 +62,10 @@ def lib():
     L.attn_decode.restype = i
     L.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i, i]
     L.attn_decode_workspace_bytes.restype = ctypes.c_size_t
+    L.attn_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, f, i32p, i, vp]
+    L.attn_decode_noalloc.restype = i
+    L.attn_decode_scratch_bytes.argtypes = []
+    L.attn_decode_scratch_bytes.restype = ctypes.c_size_t
     L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i, i, i, i, i, f, i, f, i32p, vp]
     L.attn_bwd.restype = i
     L.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
@@ -264,6 +270,42 @@ def attn_decode(q, k, v, o=None, lse=None, workspace=None, *, rope_theta=10000.0
                            _stream_handle(stream))
     if st != ATTN_OK:
         raise AttnError(st, "attn_decode")
+    return (o, lse) if lse is not None else o
+
+
+def attn_decode_scratch_bytes() -> int:
+    return int(lib().attn_decode_scratch_bytes())
+
+
+def attn_decode_noalloc(q, k, v, o, lse=None, *, rope_theta=10000.0, scale=None, window_table=None,
+                        num_splits=0, stream=None):
+    """attn_decode without a workspace and without any allocation, by this
+    wrapper or the library: the split partials live in the library's static
+    device scratch.  The caller passes the output o [B, Hq, D] (and lse
+    [B, Hq] fp32 if wanted); both are filled and o (or (o, lse)) returned.
+    Calls that overlap on one device race on the shared scratch."""
+    import torch
+    for t, n in ((k, "k"), (v, "v")):
+        _check_tensor(t, n, k)
+    B, L, Hkv, D = k.shape
+    if v.shape != k.shape:
+        raise ValueError("v must match k [B, L, Hkv, D]")
+    if (not isinstance(q, torch.Tensor) or q.dtype != torch.bfloat16 or q.dim() != 3
+            or q.shape[0] != B or q.shape[2] != D):
+        raise ValueError("q must be a bfloat16 tensor [B, Hq, D]")
+    _check_buffer(q, "q", k, torch.bfloat16)
+    Hq = q.shape[1]
+    _check_buffer(o, "o", k, torch.bfloat16, q.shape)
+    if lse is not None:
+        _check_buffer(lse, "lse", k, torch.float32, (B, Hq))
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    w, wp = _window_ptr(window_table, D)
+    st = lib().attn_decode_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                   lse.data_ptr() if lse is not None else None, B, Hq, Hkv, L, D,
+                                   float(rope_theta), float(scale), wp, int(num_splits), _stream_handle(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_decode_noalloc")
     return (o, lse) if lse is not None else o
 
 

@@ -112,6 +112,25 @@ uint16_t fp16_bits_rne(double x)
     return (uint16_t)(sign | (full >> 13));
 }
 
+// One position's row of the cos/sin table (D halves): quarter 0 holds the
+// cosines, quarter 1 the sines, pair r = 8 grp + e at half grp * 8 + e of its
+// quarter (see attn::RopeTable).  The angle is p * theta^(-2r/D) in fp64.
+void rope_inv_freq(float theta, int D, double *inv_freq)
+{
+    const double th = (double)theta;
+    for (int r = 0; r < D / 2; ++r) inv_freq[r] = std::pow(th, -2.0 * (double)r / (double)D);
+}
+void rope_row(const double *inv_freq, int D, int p, uint16_t *row)
+{
+    const int PG = D / 16;
+    for (int r = 0; r < D / 2; ++r) {
+        const double ang = (double)p * inv_freq[r];
+        const int grp = r / 8, e = r % 8;
+        row[(0 * PG + grp) * 8 + e] = fp16_bits_rne(std::cos(ang));
+        row[(1 * PG + grp) * 8 + e] = fp16_bits_rne(std::sin(ang));
+    }
+}
+
 int get_table(int dev, int D, float theta, int S, const uint16_t **out)
 {
     uint32_t bits;
@@ -123,19 +142,10 @@ int get_table(int dev, int D, float theta, int S, const uint16_t **out)
         return ATTN_OK;
     }
     const int cap = ((S + 1023) / 1024) * 1024;
-    const int PG = D / 16;
-    std::vector<uint16_t> host((size_t)cap * PG * 16);
-    const double th = (double)theta;
-    for (int r = 0; r < D / 2; ++r) {
-        const double inv_freq = std::pow(th, -2.0 * (double)r / (double)D);
-        const int grp = r / 8, e = r % 8;
-        for (int p = 0; p < cap; ++p) {
-            const double ang = (double)p * inv_freq;
-            // quarter 0 holds the cosines, quarter 1 the sines (see attn::RopeTable)
-            host[(((size_t)p * 2 + 0) * PG + grp) * 8 + e] = fp16_bits_rne(std::cos(ang));
-            host[(((size_t)p * 2 + 1) * PG + grp) * 8 + e] = fp16_bits_rne(std::sin(ang));
-        }
-    }
+    std::vector<uint16_t> host((size_t)cap * D);
+    double inv_freq[attn::kMaxPairs];
+    rope_inv_freq(theta, D, inv_freq);
+    for (int p = 0; p < cap; ++p) rope_row(inv_freq, D, p, host.data() + (size_t)p * D);
     void *dptr = nullptr;
     if (hipMalloc(&dptr, host.size() * sizeof(uint16_t)) != hipSuccess) {
         (void)hipGetLastError();
@@ -388,6 +398,7 @@ const char *attn_strerror(int status)
     case ATTN_ENOMEM: return "device allocation failed";
     case ATTN_ELAUNCH: return "HIP runtime error while launching or copying";
     case ATTN_ENODEVICE: return "no gfx950 HIP device is current";
+    case ATTN_ESCRATCH: return "the call needs more memory than the library's static scratch holds";
     default: return "unknown status";
     }
 }
@@ -464,17 +475,23 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int L, int D, int num
     return po + ml;
 }
 
-int attn_decode(const void *q, const void *k, const void *v, void *o, float *lse, void *workspace,
-                size_t workspace_bytes, int B, int Hq, int Hkv, int L, int D, float rope_theta, float scale,
-                const int32_t *window_table, int num_splits, void *stream)
+}  // extern "C"
+
+namespace {
+
+// attn_decode with the partials in `workspace` (caller-owned: size and
+// overlap checked here), or with noalloc in the library's static scratch.
+int decode_common(const void *q, const void *k, const void *v, void *o, float *lse, void *workspace,
+                  size_t workspace_bytes, int B, int Hq, int Hkv, int L, int D, float rope_theta, float scale,
+                  const int32_t *window_table, int num_splits, void *stream, bool noalloc)
 {
     int st = check_shapes(B, Hq, Hkv, L, D);
     if (st != ATTN_OK) return st;
     if (Hq / Hkv > 32) return ATTN_EUNSUPPORTED;   // query heads per KV head: one MFMA's 32 columns
     if (num_splits < 0) return ATTN_EINVAL;
     const bool empty = (B == 0 || L == 0);
-    if (!empty && (!q || !k || !v || !o || !workspace)) return ATTN_EINVAL;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(workspace))
+    if (!empty && (!q || !k || !v || !o || (!noalloc && !workspace))) return ATTN_EINVAL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (!noalloc && !aligned16(workspace)))
         return ATTN_EALIGN;
     if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return ATTN_EALIGN;
     if (!std::isfinite(scale) || !(scale > 0.0f)) return ATTN_EINVAL;
@@ -483,20 +500,26 @@ int attn_decode(const void *q, const void *k, const void *v, void *o, float *lse
     st = check_window(window_table, D, 1);
     if (st != ATTN_OK) return st;
     if (empty) return ATTN_OK;
-    if (workspace_bytes < attn_decode_workspace_bytes(B, Hq, Hkv, L, D, num_splits)) return ATTN_EINVAL;
-    const size_t nq = (size_t)B * Hq * D * 2, nkv = (size_t)B * L * Hkv * D * 2;
     const size_t nws = attn_decode_workspace_bytes(B, Hq, Hkv, L, D, num_splits);
+    if (noalloc) {
+        if (nws > attn::kDecodeScratchBytes) return ATTN_ESCRATCH;
+    } else if (workspace_bytes < nws) {
+        return ATTN_EINVAL;
+    }
+    const size_t nq = (size_t)B * Hq * D * 2, nkv = (size_t)B * L * Hkv * D * 2;
     const size_t nl = (size_t)B * Hq * 4;
-    if (overlaps(o, nq, q, nq) || overlaps(o, nq, k, nkv) || overlaps(o, nq, v, nkv) ||
-        overlaps(workspace, nws, q, nq) || overlaps(workspace, nws, k, nkv) || overlaps(workspace, nws, v, nkv) ||
-        overlaps(workspace, nws, o, nq))
+    if (overlaps(o, nq, q, nq) || overlaps(o, nq, k, nkv) || overlaps(o, nq, v, nkv))
+        return ATTN_EINVAL;
+    if (!noalloc && (overlaps(workspace, nws, q, nq) || overlaps(workspace, nws, k, nkv) ||
+                     overlaps(workspace, nws, v, nkv) || overlaps(workspace, nws, o, nq)))
         return ATTN_EINVAL;
     if (lse && (overlaps(lse, nl, q, nq) || overlaps(lse, nl, k, nkv) || overlaps(lse, nl, v, nkv) ||
-                overlaps(lse, nl, o, nq) || overlaps(lse, nl, workspace, nws)))
+                overlaps(lse, nl, o, nq) || (!noalloc && overlaps(lse, nl, workspace, nws))))
         return ATTN_EINVAL;
     int dev = -1;
     st = current_device_ok(&dev);
     if (st != ATTN_OK) return st;
+    if (noalloc && attn::decode_scratch(&workspace) != hipSuccess) return ATTN_ELAUNCH;
 
     attn::DecodeArgs a;
     std::memset(&a, 0, sizeof a);
@@ -516,12 +539,37 @@ int attn_decode(const void *q, const void *k, const void *v, void *o, float *lse
         for (int r = 0; r < D / 2; ++r) a.window[r] = window_table[r];
     }
     if (rope_theta != 0.0f) {
-        st = get_table(dev, D, rope_theta, L, &a.rope_cs);
-        if (st != ATTN_OK) return st;
+        // the query's row of the cos/sin table (position L-1), by value
+        a.use_rope = 1;
+        double inv_freq[attn::kMaxPairs];
+        rope_inv_freq(rope_theta, D, inv_freq);
+        rope_row(inv_freq, D, L - 1, a.rope_row);
     }
     if (attn::launch_decode(a, static_cast<hipStream_t>(stream)) != hipSuccess) return ATTN_ELAUNCH;
     return ATTN_OK;
 }
+
+}  // namespace
+
+extern "C" {
+
+int attn_decode(const void *q, const void *k, const void *v, void *o, float *lse, void *workspace,
+                size_t workspace_bytes, int B, int Hq, int Hkv, int L, int D, float rope_theta, float scale,
+                const int32_t *window_table, int num_splits, void *stream)
+{
+    return decode_common(q, k, v, o, lse, workspace, workspace_bytes, B, Hq, Hkv, L, D, rope_theta, scale,
+                         window_table, num_splits, stream, false);
+}
+
+int attn_decode_noalloc(const void *q, const void *k, const void *v, void *o, float *lse, int B, int Hq, int Hkv,
+                        int L, int D, float rope_theta, float scale, const int32_t *window_table, int num_splits,
+                        void *stream)
+{
+    return decode_common(q, k, v, o, lse, nullptr, 0, B, Hq, Hkv, L, D, rope_theta, scale, window_table,
+                         num_splits, stream, true);
+}
+
+size_t attn_decode_scratch_bytes(void) { return attn::kDecodeScratchBytes; }
 
 
 // Workspace of attn_bwd: the staged queries, the staged keys, Delta, then

@@ -25,7 +25,8 @@
 //    arithmetic is far from the bound).
 //  * The cache holds keys as they were stored (rotated when appended, e.g. by
 //    attn_rope_apply); with RoPE the query is rotated at position L-1 with
-//    the same table and routine as the other kernels.
+//    the same fp16 cos/sin values and routine as the other kernels (its one
+//    row travels in the kernel arguments).
 //  * With a per-pair window ("ATFlash -- Per-RoPE-Wavelength Attention
 //    Windows", "The idea") the query's pairs are masked per tile: pairs
 //    pruned on the whole tile drop out of the MFMA (and their K columns are
@@ -34,11 +35,13 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <map>
+#include <mutex>
 #include <type_traits>
 
+#include "attn_ext_args.h"
 #include "attn_gfx950.h"
 #include "attn_internal.h"
-#include "attn_ext_args.h"
 
 namespace attn {
 namespace {
@@ -91,15 +94,23 @@ __global__ __launch_bounds__(kDecWaves * 64, 1) void decode_split_kernel(const D
     // halves, half 1: their second halves), as in the prefill kernel.
     const int hq = hk * grp + (l32 % grp);
     const uint16_t *qrow = a.q + ((size_t)b * a.Hq + hq) * D;   // lane-dependent: plain global loads
-    const __amdgpu_buffer_rsrc_t cs_rs = make_rsrc(a.rope_cs, ROPE ? (uint32_t)(pos + 1) * G::ROWB : 0u);
+    // The cos/sin row of position L-1 sits in the kernel arguments (scalar
+    // loads from the argument segment).
+    typedef __attribute__((address_space(4))) const u32x4_t kconst_u4;
+    kconst_u4 *cs_row = (kconst_u4 *)((__attribute__((address_space(4))) const char *)
+                                          __builtin_amdgcn_kernarg_segment_ptr() + __builtin_offsetof(DecodeArgs, rope_row));
+    auto cs_words = [&](int i) __attribute__((always_inline)) {
+        const u32x4_t w = cs_row[i];
+        return make_uint4(w.x, w.y, w.z, w.w);
+    };
     bf16x8_t qreg[G::KCH];
 #pragma unroll
     for (int kc = 0; kc < G::KCH; ++kc) {
         uint4 lo = *reinterpret_cast<const uint4 *>(qrow + 8 * kc);
         uint4 hi = *reinterpret_cast<const uint4 *>(qrow + D / 2 + 8 * kc);
         if constexpr (ROPE) {
-            const uint4 cq = bload16(cs_rs, (uint32_t)pos * G::ROWB + 16u * kc);
-            const uint4 sq = bload16(cs_rs, (uint32_t)pos * G::ROWB + 16u * (G::PG + kc));
+            const uint4 cq = cs_words(kc);
+            const uint4 sq = cs_words(G::PG + kc);
             rope_rotate8(lo, hi, cq, sq);
         }
         qreg[kc] = __builtin_bit_cast(bf16x8_t, g == 0 ? lo : hi);
@@ -361,7 +372,7 @@ hipError_t launch_split(const DecodeArgs &a, hipStream_t stream)
 template <int D>
 hipError_t launch_d(const DecodeArgs &a, hipStream_t stream)
 {
-    const bool rope = a.rope_cs != nullptr;
+    const bool rope = a.use_rope != 0;
     hipError_t e;
     if (rope) e = a.use_window ? launch_split<D, true, true>(a, stream) : launch_split<D, true, false>(a, stream);
     else e = a.use_window ? launch_split<D, false, true>(a, stream) : launch_split<D, false, false>(a, stream);
@@ -375,6 +386,40 @@ hipError_t launch_d(const DecodeArgs &a, hipStream_t stream)
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream)
 {
     return a.D == 128 ? launch_d<128>(a, stream) : launch_d<64>(a, stream);
+}
+
+// ---- static scratch of the split partials ----------------------------------
+// For callers that cannot allocate (code under graph capture, serving loops,
+// harnesses that forbid hipMalloc): attn_decode_noalloc keeps the partial
+// outputs and (m, l) pairs here instead of in a caller workspace.  Every GPU
+// that loads the library holds its own copy until the process ends.  In host
+// code `scratch` names a host-side stand-in, not the device memory: its
+// device address is looked up once per device with hipGetSymbolAddress and
+// only that address is handed to kernels.
+namespace {
+static __device__ __align__(256) uint8_t scratch[kDecodeScratchBytes];
+std::mutex g_scratch_mu;
+std::map<int, void *> g_scratch_ptr;
+}  // namespace
+
+hipError_t decode_scratch(void **ptr)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    auto it = g_scratch_ptr.find(dev);
+    if (it == g_scratch_ptr.end()) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr) {
+            (void)hipGetLastError();
+            return e != hipSuccess ? e : hipErrorInvalidSymbol;
+        }
+        it = g_scratch_ptr.emplace(dev, p).first;
+    }
+    *ptr = it->second;
+    return hipSuccess;
 }
 
 }  // namespace attn

@@ -19,16 +19,27 @@ struct DecodeArgs {
     const uint16_t *k;        // [B, L, Hkv, D] cache
     const uint16_t *v;
     uint16_t *o;              // [B, Hq, D]
-    const uint16_t *rope_cs;  // fp16 cos/sin table (positions 0..L-1); null when RoPE is off
     float *lse;               // [B, Hq] or null
     float *part_o;            // [B, Hq, n_split, D] partial (unnormalised) outputs
     float *part_ml;           // [B, Hq, n_split, 2] partial (m, l)
     int B, Hq, Hkv, L, D;
     int n_split, keys_per_split;
     int use_window;
+    int use_rope;
     float scale_log2e;
     int32_t window[kMaxPairs];
+    // With RoPE: the fp16 cosines, then sines, of the query's position L-1,
+    // in the cos/sin table's row layout (pair group g: cos of pairs 8g..8g+7
+    // at halves 8g.., their sines at D/2 + 8g..), the same bits the table
+    // holds.  Passed by value, so decode reads no table.
+    alignas(16) uint16_t rope_row[2 * kMaxPairs];
 };
+
+// Static device scratch of the split partials for the entry point that
+// allocates nothing (attn_decode.hip): its size, and its address on the
+// current device (looked up once per device).
+constexpr size_t kDecodeScratchBytes = (size_t)32 << 20;
+hipError_t decode_scratch(void **ptr);
 
 struct BwdArgs {
     const uint16_t *q;        // [B, S, Hq, D]

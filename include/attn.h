@@ -28,8 +28,10 @@
  *  - All arguments are validated on the host before anything is enqueued;
  *    on error nothing is launched and a negative attn_status is returned.
  *  - Calls on one device from several host threads are safe; the library's
- *    only shared state is its cache of RoPE cos/sin tables and of persistent
- *    task lists, guarded by a mutex.
+ *    shared host state is its cache of RoPE cos/sin tables and of persistent
+ *    task lists, guarded by a mutex.  The one exception is
+ *    attn_decode_noalloc, whose calls share a static device buffer: calls of
+ *    it that overlap on one device race.
  */
 #ifndef ATTN_MI355X_ATTN_H
 #define ATTN_MI355X_ATTN_H
@@ -47,7 +49,8 @@ typedef enum {
     ATTN_EALIGN = -3,       /* a tensor pointer is not 16-byte aligned (lse: 4-byte) */
     ATTN_ENOMEM = -4,       /* device allocation of the cos/sin table failed */
     ATTN_ELAUNCH = -5,      /* the HIP runtime refused the launch or a copy */
-    ATTN_ENODEVICE = -6     /* no HIP device / the current device is not gfx950 */
+    ATTN_ENODEVICE = -6,    /* no HIP device / the current device is not gfx950 */
+    ATTN_ESCRATCH = -7      /* attn_decode_noalloc: the partials exceed the static scratch */
 } attn_status;
 
 /*
@@ -165,6 +168,8 @@ long long attn_persistent_schedule(int B, int Hq, int S, int bins, uint32_t *out
  *  num_splits: 0 lets the library choose (about 1024 waves over the batch,
  *      at least 64 keys per split); k > 0 asks for k splits (at most one per
  *      32 keys, at most 1024).  Errors as for attn_fwd.
+ *  The query's cos/sin row travels by value in the kernel arguments: decode
+ *  reads and allocates no table.
  */
 size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int L, int D, int num_splits);
 int attn_decode(const void *q, const void *k, const void *v, void *o, float *lse,
@@ -172,6 +177,33 @@ int attn_decode(const void *q, const void *k, const void *v, void *o, float *lse
                 int B, int Hq, int Hkv, int L, int D,
                 float rope_theta, float scale, const int32_t *window_table,
                 int num_splits, void *stream);
+
+/*
+ * attn_decode for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  It
+ * runs the same kernels with the same arguments (and returns the same o and
+ * lse bit for bit) but keeps the split partials in a static device buffer
+ * of the library instead of a caller workspace, and calls no allocating
+ * routine.  The caller still owns q, k, v, o and lse.
+ *
+ *  Limit: the partials take attn_decode_workspace_bytes(B, Hq, Hkv, L, D,
+ *      num_splits) bytes, about B * Hq * splits * (4 D + 8); they must fit in
+ *      attn_decode_scratch_bytes() (32 MiB).  Larger calls return
+ *      ATTN_ESCRATCH and launch nothing.  For example the Llama-3-70B head
+ *      shape (Hq 64, Hkv 8, D 128) with the default split plan needs 4.1 MiB
+ *      at B = 1 and at B = 8.
+ *  Sharing: each device holds one such buffer (it lives until the process
+ *      ends), shared by every call on that device and left holding the last
+ *      call's partials.  Calls that overlap on one device (concurrent streams
+ *      or host threads) race on it; calls ordered on one stream do not.  The
+ *      kernels write every partial they read, so nothing needs clearing.
+ *  Other arguments and errors as attn_decode.
+ */
+int attn_decode_noalloc(const void *q, const void *k, const void *v, void *o, float *lse,
+                        int B, int Hq, int Hkv, int L, int D,
+                        float rope_theta, float scale, const int32_t *window_table,
+                        int num_splits, void *stream);
+size_t attn_decode_scratch_bytes(void);
 
 /*
  * Attention backward: the gradients of the attn_fwd loss with respect to q,

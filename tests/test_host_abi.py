@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_strerror_covers_every_status():
-    for st in range(0, -7, -1):
+    for st in range(0, -8, -1):
         msg = binding.strerror(st)
         assert msg and msg != "unknown status"
     assert binding.strerror(-99) == "unknown status"
@@ -360,3 +360,32 @@ def test_binding_rejects_host_tensors_before_any_call():
         binding.attn_decode(q[:, 0].contiguous(), q, q)
     with pytest.raises(TypeError):
         binding.attn_bwd(q, q, q, q, torch.zeros(1, 2, 64), q)
+
+
+def _dec_noalloc_call(**kw):
+    a = dict(q=A, k=A * 64, v=A * 128, o=A * 192, lse=None, B=1, Hq=8, Hkv=2, L=100, D=128, theta=1e4,
+             scale=0.088, w=None, ns=0)
+    a.update(kw)
+    return binding.lib().attn_decode_noalloc(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                                             a["L"], a["D"], a["theta"], a["scale"], a["w"], a["ns"], None)
+
+
+def test_decode_noalloc_limits_and_errors():
+    """The no-allocation decode takes the split partials from a static
+    buffer of attn_decode_scratch_bytes(); a call that needs more is
+    rejected on the host (ATTN_ESCRATCH) before any device work, and the
+    argument errors are attn_decode's."""
+    cap = binding.attn_decode_scratch_bytes()
+    assert cap == 32 << 20
+    # the library's own split plan fits the scratch for the supported groupings
+    for B, Hq, Hkv, L, D in ((1, 64, 8, 32768, 128), (8, 64, 8, 32768, 128), (1, 32, 1, 1 << 20, 128),
+                             (64, 64, 2, 4096, 128), (3, 12, 12, 77, 64)):
+        assert binding.attn_decode_workspace_bytes(B, Hq, Hkv, L, D, 0) <= cap
+    big = dict(B=64, Hq=64, Hkv=8, L=32768, D=128, ns=1024)
+    assert binding.attn_decode_workspace_bytes(64, 64, 8, 32768, 128, 1024) > cap
+    assert _dec_noalloc_call(**big) == binding.ATTN_ESCRATCH
+    assert _dec_noalloc_call(Hq=66, Hkv=2) == binding.ATTN_EUNSUPPORTED
+    assert _dec_noalloc_call(q=A + 8) == binding.ATTN_EALIGN
+    assert _dec_noalloc_call(o=A) == binding.ATTN_EINVAL
+    assert _dec_noalloc_call(scale=-1.0) == binding.ATTN_EINVAL
+    assert _dec_noalloc_call(B=0) == binding.ATTN_OK

@@ -19,7 +19,6 @@ against both rules.
 """
 import os
 import re
-import shutil
 import subprocess
 import tempfile
 
@@ -43,21 +42,50 @@ def _writes(ops):
     return ops[0] if ops else ""
 
 
+def code_objects(lib_path):
+    """The gfx950 code objects of a built library: its .hip_fatbin section
+    holds one offload bundle per HIP source file (magic, entry count, then
+    offset / size / target triple per entry, offsets from the bundle's
+    start)."""
+    import struct
+    with tempfile.TemporaryDirectory() as d:
+        fat = os.path.join(d, "fatbin.bin")
+        subprocess.run(["objcopy", "-O", "binary", "--only-section=.hip_fatbin", lib_path, fat], check=True)
+        with open(fat, "rb") as f:
+            data = f.read()
+    magic = b"__CLANG_OFFLOAD_BUNDLE__"
+    out, pos = [], 0
+    while True:
+        i = data.find(magic, pos)
+        if i < 0:
+            break
+        (n,) = struct.unpack_from("<Q", data, i + len(magic))
+        off = i + len(magic) + 8
+        for _ in range(n):
+            o, size, tlen = struct.unpack_from("<QQQ", data, off)
+            off += 24
+            triple = data[off:off + tlen].decode()
+            off += tlen
+            if triple.endswith("gfx950") and size > 0:
+                out.append(data[i + o:i + o + size])
+        pos = i + len(magic)
+    return out
+
+
 def _disassembly():
     if not os.path.exists(binding.LIB_PATH):
         pytest.skip("library not built")
-    for tool in ("clang-offload-bundler", "llvm-objdump"):
-        if not os.path.exists(os.path.join(LLVM, tool)):
-            pytest.skip("ROCm LLVM tools not found")
+    if not os.path.exists(os.path.join(LLVM, "llvm-objdump")):
+        pytest.skip("ROCm LLVM tools not found")
+    texts = []
     with tempfile.TemporaryDirectory() as d:
-        fat = os.path.join(d, "fatbin.bin")
-        co = os.path.join(d, "code.co")
-        subprocess.run(["objcopy", "-O", "binary", "--only-section=.hip_fatbin", binding.LIB_PATH, fat], check=True)
-        subprocess.run([os.path.join(LLVM, "clang-offload-bundler"), "--type=o", "--input=" + fat,
-                        "--targets=hipv4-amdgcn-amd-amdhsa--gfx950", "--output=" + co, "--unbundle"], check=True)
-        out = subprocess.run([os.path.join(LLVM, "llvm-objdump"), "-d", "--mcpu=gfx950", co],
-                             check=True, capture_output=True, text=True).stdout
-    return out
+        for j, co in enumerate(code_objects(binding.LIB_PATH)):
+            path = os.path.join(d, "code%d.co" % j)
+            with open(path, "wb") as f:
+                f.write(co)
+            texts.append(subprocess.run([os.path.join(LLVM, "llvm-objdump"), "-d", "--mcpu=gfx950", path],
+                                        check=True, capture_output=True, text=True).stdout)
+    return "\n".join(texts)
 
 
 def _scan(text):
@@ -112,6 +140,17 @@ def test_scanner_flags_a_planted_hazard():
     assert len(found) == 2
     assert found[0][3] == 1 and "s41" in found[0][2]
     assert "m0" in found[1][2]
+
+
+def test_every_source_file_is_scanned():
+    """One code object per HIP source file, and the direct-to-LDS loads of
+    the forward, decode and backward kernels are all in the scan."""
+    text = _disassembly()
+    assert len(code_objects(binding.LIB_PATH)) == 4
+    for kernel in ("attn_fwd_kernel", "decode_split_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"):
+        assert kernel in text, kernel
+    loads = [l for l in text.split("\n") if "buffer_load" in l and " lds" in l]
+    assert len(loads) > 700, len(loads)
 
 
 def test_lds_dma_wait_states():
