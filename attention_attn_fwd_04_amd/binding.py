@@ -25,7 +25,8 @@ ATTN_ELAUNCH = -5
 ATTN_ENODEVICE = -6
 ATTN_ESCRATCH = -7
 
-EXPORTED = ("attn_fwd", "attn_fwd_lse", "attn_fwd_persistent", "attn_persistent_schedule", "attn_decode",
+EXPORTED = ("attn_fwd", "attn_fwd_lse", "attn_fwd_persistent", "attn_fwd_rotated_k", "attn_persistent_schedule",
+            "attn_decode",
             "attn_decode_workspace_bytes", "attn_decode_noalloc", "attn_decode_scratch_bytes", "attn_bwd",
             "attn_bwd_workspace_bytes", "attn_rope_apply", "attn_window_table", "attn_pruned_terms",
             "attn_check_args", "attn_strerror", "attn_release")
@@ -56,6 +57,8 @@ def lib():
     L.attn_fwd_lse.restype = i
     L.attn_fwd_persistent.argtypes = [vp, vp, vp, vp, i, i, i, i, i, f, i, f, i32p, vp]
     L.attn_fwd_persistent.restype = i
+    L.attn_fwd_rotated_k.argtypes = [vp, vp, vp, vp, i, i, i, i, i, f, i, f, i32p, vp]
+    L.attn_fwd_rotated_k.restype = i
     L.attn_persistent_schedule.argtypes = [i, i, i, i, ctypes.POINTER(ctypes.c_uint32), ctypes.c_longlong]
     L.attn_persistent_schedule.restype = ctypes.c_longlong
     L.attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i, i, i, i, i, f, f, i32p, i, vp]
@@ -151,6 +154,13 @@ def attn_fwd_persistent(q, k, v, o=None, *, rope_theta=10000.0, causal=True, sca
     """attn_fwd on the persistent, cost-balanced schedule of the causal query
     tiles; returns o [B,S,Hq,D] (bitwise equal to attn_fwd's)."""
     return _fwd("attn_fwd_persistent", q, k, v, o, rope_theta, causal, scale, window_table, stream)
+
+
+def attn_fwd_rotated_k(q, k_rot, v, o=None, *, rope_theta=10000.0, causal=True, scale=None,
+                       window_table=None, stream=None):
+    """attn_fwd with the query rotated at load and keys already rotated
+    (attn_rope_apply(None, k)); returns o [B,S,Hq,D], bitwise attn_fwd's."""
+    return _fwd("attn_fwd_rotated_k", q, k_rot, v, o, rope_theta, causal, scale, window_table, stream)
 
 
 def attn_persistent_schedule(B, Hq, S, bins):
@@ -354,21 +364,30 @@ def attn_bwd(q, k, v, o, lse, dout, dq=None, dk=None, dv=None, workspace=None, *
 
 
 def attn_rope_apply(q, k, q_out=None, k_out=None, *, rope_theta=10000.0, stream=None):
-    """Separate RoPE pass: rotated copies (q_out, k_out) of q and k."""
+    """Separate RoPE pass: rotated copies (q_out, k_out) of q and k.  With
+    q None only the keys are rotated (q_out is then None)."""
     import torch
-    _check_tensor(q, "q", q)
-    _check_tensor(k, "k", q)
-    B, S, Hq, D = q.shape
-    Hkv = k.shape[2]
-    if k.shape != (B, S, Hkv, D):
-        raise ValueError("k must be [B, S, Hkv, D] matching q")
-    q_out = torch.empty_like(q) if q_out is None else q_out
+    _check_tensor(k, "k", k)
+    B, S, Hkv, D = k.shape
+    if q is not None:
+        _check_tensor(q, "q", k)
+        Hq = q.shape[2]
+        if q.shape != (B, S, Hq, D):
+            raise ValueError("k must be [B, S, Hkv, D] matching q")
+        q_out = torch.empty_like(q) if q_out is None else q_out
+        _check_tensor(q_out, "q_out", k)
+        if q_out.shape != q.shape:
+            raise ValueError("q_out must be shaped like q")
+    else:
+        if q_out is not None:
+            raise ValueError("q_out without q")
+        Hq = Hkv
     k_out = torch.empty_like(k) if k_out is None else k_out
-    _check_tensor(q_out, "q_out", q)
-    _check_tensor(k_out, "k_out", q)
-    if q_out.shape != q.shape or k_out.shape != k.shape:
-        raise ValueError("q_out and k_out must be shaped like q and k")
-    st = lib().attn_rope_apply(q.data_ptr(), k.data_ptr(), q_out.data_ptr(), k_out.data_ptr(),
+    _check_tensor(k_out, "k_out", k)
+    if k_out.shape != k.shape:
+        raise ValueError("k_out must be shaped like k")
+    st = lib().attn_rope_apply(q.data_ptr() if q is not None else None, k.data_ptr(),
+                               q_out.data_ptr() if q is not None else None, k_out.data_ptr(),
                                B, Hq, Hkv, S, D, float(rope_theta), _stream_handle(stream))
     if st != ATTN_OK:
         raise AttnError(st, "attn_rope_apply")

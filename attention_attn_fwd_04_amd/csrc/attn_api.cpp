@@ -308,10 +308,11 @@ int check_window(const int32_t *w, int D, int causal)
 
 int fwd_common(const void *q, const void *k, const void *v, void *o, float *lse, int B, int Hq, int Hkv, int S,
                int D, float rope_theta, int causal, float scale, const int32_t *window_table, void *stream,
-               bool persistent = false)
+               bool persistent = false, bool k_rotated = false)
 {
     int st = attn_check_args(q, k, v, o, B, Hq, Hkv, S, D, rope_theta, causal, scale, window_table);
     if (st != ATTN_OK) return st;
+    if (k_rotated && rope_theta == 0.0f) return ATTN_EINVAL;   // the query is rotated: theta > 1
     if (persistent && (window_table != nullptr || !sched_fits(B, Hq, S))) return ATTN_EUNSUPPORTED;
     int dev = -1;
     st = current_device_ok(&dev);
@@ -335,6 +336,7 @@ int fwd_common(const void *q, const void *k, const void *v, void *o, float *lse,
     if (rope_theta != 0.0f) {
         st = get_table(dev, D, rope_theta, S, &a.rope_cs);
         if (st != ATTN_OK) return st;
+        a.rope_k = k_rotated ? 0 : 1;
     }
     if (persistent && causal) {
         st = get_schedule(dev, B, Hq, S, &a.sched, &a.sched_bins);
@@ -450,6 +452,13 @@ int attn_fwd_persistent(const void *q, const void *k, const void *v, void *o, in
                         float rope_theta, int causal, float scale, const int32_t *window_table, void *stream)
 {
     return fwd_common(q, k, v, o, nullptr, B, Hq, Hkv, S, D, rope_theta, causal, scale, window_table, stream, true);
+}
+
+int attn_fwd_rotated_k(const void *q, const void *k_rot, const void *v, void *o, int B, int Hq, int Hkv, int S,
+                       int D, float rope_theta, int causal, float scale, const int32_t *window_table, void *stream)
+{
+    return fwd_common(q, k_rot, v, o, nullptr, B, Hq, Hkv, S, D, rope_theta, causal, scale, window_table, stream,
+                      false, true);
 }
 
 long long attn_persistent_schedule(int B, int Hq, int S, int bins, uint32_t *out, long long cap)
@@ -664,12 +673,16 @@ int attn_rope_apply(const void *q, const void *k, void *q_out, void *k_out, int 
     int st = check_shapes(B, Hq, Hkv, S, D);
     if (st != ATTN_OK) return st;
     const bool empty = (B == 0 || S == 0);
-    if (!empty && (!q || !k || !q_out || !k_out)) return ATTN_EINVAL;
+    // q and q_out both NULL: rotate the keys only.
+    if ((q == nullptr) != (q_out == nullptr)) return ATTN_EINVAL;
+    const bool with_q = q != nullptr;
+    if (!empty && (!k || !k_out)) return ATTN_EINVAL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(q_out) || !aligned16(k_out)) return ATTN_EALIGN;
     if (rope_theta == 0.0f || check_theta(rope_theta) != ATTN_OK) return ATTN_EINVAL;
-    const size_t nq = (size_t)B * S * Hq * D * 2, nk = (size_t)B * S * Hkv * D * 2;
-    if (!empty && (overlaps(q_out, nq, q, nq) || overlaps(q_out, nq, k, nk) || overlaps(k_out, nk, q, nq) ||
-                   overlaps(k_out, nk, k, nk) || overlaps(q_out, nq, k_out, nk)))
+    const size_t nq = with_q ? (size_t)B * S * Hq * D * 2 : 0, nk = (size_t)B * S * Hkv * D * 2;
+    if (!empty && (overlaps(k_out, nk, k, nk) ||
+                   (with_q && (overlaps(q_out, nq, q, nq) || overlaps(q_out, nq, k, nk) ||
+                               overlaps(k_out, nk, q, nq) || overlaps(q_out, nq, k_out, nk)))))
         return ATTN_EINVAL;
     int dev = -1;
     st = current_device_ok(&dev);

@@ -80,7 +80,8 @@ constexpr int kBN = 64;                     // keys per iteration (two 32-key bl
 constexpr float kLazyMaxSum = 16384.0f;     // lazy rescale: partial row sums of P stay <= 2^14
 constexpr int kBandTiles = 64;              // query tiles per band of heads in the work order
 
-template <int D, bool ROPE>
+// CS: the tiles carry a cos/sin ring (keys rotated in LDS).
+template <int D, bool CS>
 struct Geo {
     static constexpr int KCH = D / 16;      // MFMA k-steps over D (8 pairs each)
     static constexpr int PG = D / 16;       // 8-pair groups per row
@@ -96,7 +97,7 @@ struct Geo {
     static constexpr int KRING = 0;
     static constexpr int VRING = KSLOTS * TILE_B;
     static constexpr int CRING = VRING + VSLOTS * TILE_B;
-    static constexpr int RING_BYTES = CRING + (ROPE ? CSLOTS * TILE_B : 0);
+    static constexpr int RING_BYTES = CRING + (CS ? CSLOTS * TILE_B : 0);
     static constexpr int QP_B = ROWB + 16;                // padded Q staging rows
     static constexpr int Q_BYTES = kBM * QP_B;
     static constexpr int LDS_BYTES = (RING_BYTES > Q_BYTES) ? RING_BYTES : Q_BYTES;
@@ -118,10 +119,14 @@ struct Geo {
 // PERSIST false: one work-group per query tile (work decoded from the block
 // index).  PERSIST true: one work-group per compute unit, running the query
 // tiles of its bin in a host-built task list, one after the other.
-template <int D, bool ROPE, bool CAUSAL, bool WINDOW, bool PERSIST>
+// ROPE: the query is rotated at load.  ROPE_K: each key tile is rotated in
+// LDS as well (fused RoPE); without it the keys arrive rotated (a separate
+// pass rotated them) and the cos/sin stream and its ring are not used.
+template <int D, bool ROPE, bool ROPE_K, bool CAUSAL, bool WINDOW, bool PERSIST>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
 {
-    using G = Geo<D, ROPE>;
+    static_assert(ROPE || !ROPE_K, "keys are rotated in the kernel only with the query");
+    using G = Geo<D, ROPE_K>;
     __shared__ __attribute__((aligned(16))) uint8_t smem[G::LDS_BYTES];
 
     const int tid = threadIdx.x;
@@ -148,7 +153,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
         // K, V and the cos/sin table for the direct-to-LDS loads.
         const u32x4_t k_rs = make_desc(a.k + ((size_t)b * S * a.Hkv + hk) * D, (uint32_t)S * kv_rowb);
         const u32x4_t v_rs = make_desc(a.v + ((size_t)b * S * a.Hkv + hk) * D, (uint32_t)S * kv_rowb);
-        const u32x4_t cs_desc = make_desc(a.rope_cs, ROPE ? (uint32_t)S * G::ROWB : 0u);
+        const u32x4_t cs_desc = make_desc(a.rope_cs, ROPE_K ? (uint32_t)S * G::ROWB : 0u);
         uint16_t *og = a.o + ((size_t)b * S * a.Hq + hq) * D;
 
         // ---- Q tile: load, rotate, stage through LDS into B-operand registers --
@@ -237,14 +242,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
         };
         auto dload_k = [&](int t) __attribute__((always_inline)) {
             dload(k_rs, kv_rowb, kslot32(t), t, lane_k);
-            if constexpr (ROPE) dload(cs_desc, (uint32_t)G::ROWB, cslot32(t), t, lane_c);
+            if constexpr (ROPE_K) dload(cs_desc, (uint32_t)G::ROWB, cslot32(t), t, lane_c);
         };
         auto dload_v = [&](int t) __attribute__((always_inline)) { dload(v_rs, kv_rowb, vslot32(t), t, lane_v); };
         // Loads of iteration i, one 1 KB instruction per step: V(i+1), K(i+3)
         // and, with RoPE, the cos/sin rows of K(i+3).  They are issued in every
         // iteration: tiles past the end read as zeros into slots that are free
         // and never read again, which keeps the wait counts constant.
-        constexpr int NDMA = G::NI_W * (ROPE ? 3 : 2);
+        constexpr int NDMA = G::NI_W * (ROPE_K ? 3 : 2);
         auto dma_step = [&](int i, int j) __attribute__((always_inline)) {
             const int which = j / G::NI_W, jj = j % G::NI_W;
             const uint32_t dst = (uint32_t)((wave + kWaves * jj) * 1024);
@@ -264,7 +269,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
         const int r_key = lane, r_pg = wave;
         const int w_rot = WINDOW ? wtab[8 * r_pg + 7] : 0;   // widest window of the pair group
         auto rotate_k = [&](int t) __attribute__((always_inline)) {
-            if constexpr (ROPE) {
+            if constexpr (ROPE_K) {
                 if (wave * 64 < G::K_UNITS) {   // K_UNITS is a multiple of 64: wave-uniform
                     if constexpr (WINDOW) {
                         const int dmin = max(0, n0 - (t * kBN + kBN - 1));
@@ -433,6 +438,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
 
         // Block 1: S(i) = K'(i) Q'^T; with ROT, rotation of this thread's unit of
         // K(i+1) spread over the MFMAs (one 32-bit word of each half at a time).
+        // The unit's LDS reads go out after the first K operand reads (LDS
+        // requests complete in order: issued first, they would hold up the
+        // first MFMA) and are first used a few MFMAs later.
         auto block1 = [&](auto rot_c, int i) __attribute__((always_inline)) {
             constexpr bool ROT = decltype(rot_c)::value;
             f32x16_t minit;   // -m_ref: the start of both QK chains
@@ -452,19 +460,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
             uint4 rlo, rhi, rcq, rsq;
             uint8_t *rks = kslot(i + 1);
             const int o_lo = G::k_off(r_key, r_pg), o_hi = G::k_off(r_key, G::PG + r_pg);
-            if constexpr (ROT) {
-                const uint8_t *rcs = cslot(i + 1);
-                rlo = lds_at<uint4>(rks, o_lo);
-                rhi = lds_at<uint4>(rks, o_hi);
-                rcq = lds_at<uint4>(const_cast<uint8_t *>(rcs), o_lo);
-                rsq = lds_at<uint4>(const_cast<uint8_t *>(rcs), o_hi);
-            }
 #pragma unroll
             for (int k = 0; k < PF; ++k) kread(k);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int k = 0; k < NM1; ++k) {
                 if (k + PF < NM1) kread(k + PF);
+                if constexpr (ROT) {
+                    if (k == 0) {
+                        const uint8_t *rcs = cslot(i + 1);
+                        rlo = lds_at<uint4>(rks, o_lo);
+                        rhi = lds_at<uint4>(rks, o_hi);
+                        rcq = lds_at<uint4>(const_cast<uint8_t *>(rcs), o_lo);
+                        rsq = lds_at<uint4>(const_cast<uint8_t *>(rcs), o_hi);
+                    }
+                }
                 {
                     constexpr int EVERY_DMA = (NM1 - 2) / NDMA;
                     if (k % EVERY_DMA == 1 && k / EVERY_DMA < NDMA) dma_step(i, k / EVERY_DMA);
@@ -476,12 +486,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
                     sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[k], qreg[kc], sc[kb], 0, 0, 0);
                 }
                 if constexpr (ROT) {
-                    constexpr int EVERY = NM1 / 4;
-                    if (k % EVERY == EVERY - 1) {
-                        uint32_t &l = (k / EVERY == 0) ? rlo.x : (k / EVERY == 1) ? rlo.y : (k / EVERY == 2) ? rlo.z : rlo.w;
-                        uint32_t &h = (k / EVERY == 0) ? rhi.x : (k / EVERY == 1) ? rhi.y : (k / EVERY == 2) ? rhi.z : rhi.w;
-                        uint32_t cw = (k / EVERY == 0) ? rcq.x : (k / EVERY == 1) ? rcq.y : (k / EVERY == 2) ? rcq.z : rcq.w;
-                        uint32_t sw = (k / EVERY == 0) ? rsq.x : (k / EVERY == 1) ? rsq.y : (k / EVERY == 2) ? rsq.z : rsq.w;
+                    constexpr int R0 = NM1 / 4 + 1, RS = (NM1 - 1 - R0) / 3;   // words at R0 + RS r
+                    if (k >= R0 && (k - R0) % RS == 0 && (k - R0) / RS < 4) {
+                        const int wr = (k - R0) / RS;
+                        uint32_t &l = (wr == 0) ? rlo.x : (wr == 1) ? rlo.y : (wr == 2) ? rlo.z : rlo.w;
+                        uint32_t &h = (wr == 0) ? rhi.x : (wr == 1) ? rhi.y : (wr == 2) ? rhi.z : rhi.w;
+                        uint32_t cw = (wr == 0) ? rcq.x : (wr == 1) ? rcq.y : (wr == 2) ? rcq.z : rcq.w;
+                        uint32_t sw = (wr == 0) ? rsq.x : (wr == 1) ? rsq.y : (wr == 2) ? rsq.z : rsq.w;
                         rope_rotate_word(l, h, cw, sw);
                         asm volatile("" : "+v"(l), "+v"(h));
                     }
@@ -526,13 +537,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
             uint4 rlo, rhi, rcq, rsq;
             uint8_t *rks = kslot(i + 1);
             const int o_lo = G::k_off(r_key, r_pg), o_hi = G::k_off(r_key, G::PG + r_pg);
-            if constexpr (ROT) {
-                const uint8_t *rcs = cslot(i + 1);
-                rlo = lds_at<uint4>(rks, o_lo);
-                rhi = lds_at<uint4>(rks, o_hi);
-                rcq = lds_at<uint4>(const_cast<uint8_t *>(rcs), o_lo);
-                rsq = lds_at<uint4>(const_cast<uint8_t *>(rcs), o_hi);
-            }
             WordMask msk[2][2];   // chunks NS, NS + 1 of each block
             if constexpr (!GEN) {
 #pragma unroll
@@ -546,6 +550,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
 #pragma unroll
             for (int k = 0; k < NM; ++k) {
                 if (k + PF < NM) kread(k + PF);
+                if constexpr (ROT) {
+                    if (k == 0) {   // after the first operand reads, as in block 1
+                        const uint8_t *rcs = cslot(i + 1);
+                        rlo = lds_at<uint4>(rks, o_lo);
+                        rhi = lds_at<uint4>(rks, o_hi);
+                        rcq = lds_at<uint4>(const_cast<uint8_t *>(rcs), o_lo);
+                        rsq = lds_at<uint4>(const_cast<uint8_t *>(rcs), o_hi);
+                    }
+                }
 #pragma unroll
                 for (int j = 0; j < NDMA; ++j)
                     if (j * NM / NDMA == k) dma_step(i, j);
@@ -664,7 +677,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
         // With a window, a pair group pruned on the whole work-group tile is
         // never read, so it is not rotated.
         auto rot_on = [&](int i) __attribute__((always_inline)) {
-            return ROPE && i + 1 < T && wave * 64 < G::K_UNITS &&
+            return ROPE_K && i + 1 < T && wave * 64 < G::K_UNITS &&
                    !(WINDOW && w_rot < max(0, n0 - ((i + 1) * kBN + kBN - 1)));
         };
         // S(i) into sc, with K(i+1) rotated alongside.
@@ -755,7 +768,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
         dload_v(0);
         wait_vmcnt<0>();
         __syncthreads();
-        if constexpr (ROPE) {
+        if constexpr (ROPE_K) {
             rotate_k(0);
             __syncthreads();
         }
@@ -866,7 +879,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
     }
 }
 
-template <int D, bool ROPE, bool CAUSAL, bool WINDOW>
+template <int D, bool ROPE, bool ROPE_K, bool CAUSAL, bool WINDOW>
 hipError_t launch_t(const FwdArgs &a, hipStream_t stream)
 {
     const int n_qt = (a.S + kBM - 1) / kBM;
@@ -876,29 +889,34 @@ hipError_t launch_t(const FwdArgs &a, hipStream_t stream)
         // Persistent: one work-group per bin of the task list (causal, no
         // window: without the mask every query tile costs the same).
         if constexpr (CAUSAL && !WINDOW)
-            hipLaunchKernelGGL((attn_fwd_kernel<D, ROPE, CAUSAL, WINDOW, true>), dim3((unsigned)a.sched_bins),
+            hipLaunchKernelGGL((attn_fwd_kernel<D, ROPE, ROPE_K, CAUSAL, WINDOW, true>), dim3((unsigned)a.sched_bins),
                                dim3(kThreads), 0, stream, a);
         else
             return hipErrorInvalidValue;
     } else {
-        hipLaunchKernelGGL((attn_fwd_kernel<D, ROPE, CAUSAL, WINDOW, false>), dim3((unsigned)n_work), dim3(kThreads),
+        hipLaunchKernelGGL((attn_fwd_kernel<D, ROPE, ROPE_K, CAUSAL, WINDOW, false>), dim3((unsigned)n_work), dim3(kThreads),
                            0, stream, a);
     }
     return hipGetLastError();
 }
 
-template <int D>
-hipError_t launch_d(const FwdArgs &a, hipStream_t stream)
+template <int D, bool ROPE, bool ROPE_K>
+hipError_t launch_c(const FwdArgs &a, hipStream_t stream)
 {
-    const bool rope = a.rope_cs != nullptr;
     if (a.use_window) {
         // The window is defined on the causal triangle only (checked by the host API).
         if (!a.causal) return hipErrorInvalidValue;
-        return rope ? launch_t<D, true, true, true>(a, stream) : launch_t<D, false, true, true>(a, stream);
+        return launch_t<D, ROPE, ROPE_K, true, true>(a, stream);
     }
-    if (rope)
-        return a.causal ? launch_t<D, true, true, false>(a, stream) : launch_t<D, true, false, false>(a, stream);
-    return a.causal ? launch_t<D, false, true, false>(a, stream) : launch_t<D, false, false, false>(a, stream);
+    return a.causal ? launch_t<D, ROPE, ROPE_K, true, false>(a, stream)
+                    : launch_t<D, ROPE, ROPE_K, false, false>(a, stream);
+}
+
+template <int D>
+hipError_t launch_d(const FwdArgs &a, hipStream_t stream)
+{
+    if (a.rope_cs == nullptr) return launch_c<D, false, false>(a, stream);
+    return a.rope_k ? launch_c<D, true, true>(a, stream) : launch_c<D, true, false>(a, stream);
 }
 
 }  // namespace

@@ -28,6 +28,7 @@ struct FwdArgs {
     const uint16_t *v;
     uint16_t *o;
     const uint16_t *rope_cs;  // fp16 cos/sin table; null when RoPE is off
+    int rope_k;               // with RoPE: 1 rotates the keys in the kernel, 0 takes them rotated
     float *lse;               // [B, Hq, S] natural-log LSE of each row's scores; null: not written
     int B, Hq, Hkv, S, D;
     int causal;

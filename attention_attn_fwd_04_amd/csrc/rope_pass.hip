@@ -6,7 +6,8 @@
 // row (reads 2 x 16 bytes of the row and the two 16-byte cos/sin quarters of its
 // position, writes 2 x 16 bytes), using the same rotation routine and table
 // as the fused kernel so both produce identical bf16 bits.  Rows of Q and of
-// K are numbered together, Q rows first; a row is (b, s, h) in BSHD order, so
+// K are numbered together, Q rows first (without a query, only the keys are
+// rotated); a row is (b, s, h) in BSHD order, so
 // consecutive threads walk contiguous memory and the heads of one position
 // share one cos/sin line in cache.
 #include <hip/hip_runtime.h>
@@ -48,7 +49,7 @@ template <int D>
 hipError_t launch_d(const RopeArgs &a, hipStream_t stream)
 {
     constexpr int PG = D / 16;
-    const long long rows_q = (long long)a.B * a.S * a.Hq;
+    const long long rows_q = a.q != nullptr ? (long long)a.B * a.S * a.Hq : 0;   // q NULL: keys only
     const long long rows_k = (long long)a.B * a.S * a.Hkv;
     const long long n_q_units = rows_q * PG;
     const long long n_units = (rows_q + rows_k) * PG;

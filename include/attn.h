@@ -129,6 +129,25 @@ int attn_fwd_persistent(const void *q, const void *k, const void *v, void *o,
                         const int32_t *window_table, void *stream);
 
 /*
+ * attn_fwd with RoPE for keys that are already rotated: the query is rotated
+ * at load as in attn_fwd, the keys k_rot [B,S,Hkv,D] are taken as R(m) k
+ * (attn_rope_apply with q = q_out = NULL writes them), so the key tiles are
+ * neither rotated nor accompanied by cos/sin tiles in the kernel.  This is
+ * "AttnFuse" section 5.3's fuse-or-pre-rotate choice made per operand: the
+ * query's rotation costs one pass over Q per work-group wherever it is done,
+ * while the keys' rotation inside the kernel is repeated for every query
+ * tile that reads them (the O(N^2 D / BM) term of the crossover), against one
+ * O(N D) pass outside it.  With keys from that pass, o is bitwise attn_fwd's.
+ *
+ *  rope_theta must be > 1 (the query's rotation); other arguments, layout and
+ *  errors as attn_fwd.
+ */
+int attn_fwd_rotated_k(const void *q, const void *k_rot, const void *v, void *o,
+                       int B, int Hq, int Hkv, int S, int D,
+                       float rope_theta, int causal, float scale,
+                       const int32_t *window_table, void *stream);
+
+/*
  * The task list attn_fwd_persistent uses for (B, Hq, S) over `bins` bins
  * (min(bins, task count) are used), written to the HOST array out:
  * out[0 .. bins'] the bin offsets, then the tasks qt | hq << 12 | b << 22 bin
@@ -252,7 +271,8 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *o, const v
  * after scaling it by scale * log2 e, attn_fwd(rope_theta = 0) on q_out
  * rounds it a second time, so the two paths agree to that rounding).
  * q_out/k_out are caller-owned workspaces that must not overlap the inputs.
- * rope_theta must be > 1.
+ * q and q_out may both be NULL: then only the keys are rotated (for
+ * attn_fwd_rotated_k).  rope_theta must be > 1.
  */
 int attn_rope_apply(const void *q, const void *k, void *q_out, void *k_out,
                     int B, int Hq, int Hkv, int S, int D, float rope_theta,

@@ -250,3 +250,64 @@ def test_separate_path_full_size_sampled(name):
     ref = O.attn_rows(bf16_bits(q), bf16_bits(k), bf16_bits(v), rows, theta, True, scale, None)
     assert_parity(o, ref, rows=rows, label="separate " + name)
     assert torch.isfinite(o.float()).all()
+
+
+# ---------------------------------------------------------------------------
+# Query rotated at load, keys rotated by the pass beforehand
+# (attn_rope_apply with the keys only, then attn_fwd_rotated_k): the pass's
+# keys are the fused kernel's K' bit for bit and the query takes the fused
+# kernel's path, so the output is bitwise attn_fwd's.
+# ---------------------------------------------------------------------------
+def run_rotated_k(q, k, v, theta, causal, scale, window=None):
+    qd, kd, vd = _gpu(q, k, v)
+    _, kr = binding.attn_rope_apply(None, kd, rope_theta=theta)
+    o = binding.attn_fwd_rotated_k(qd, kr, vd, rope_theta=theta, causal=causal, scale=scale, window_table=window)
+    torch.cuda.synchronize()
+    return o.cpu()
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,S,D,theta,causal", [c for c in CASES if c[5] > 0])
+def test_rotated_k_is_bitwise_fused(B, Hq, Hkv, S, D, theta, causal):
+    q, k, v = make_qkv(B, S, Hq, Hkv, D, seed=2500 + S)
+    scale = 1 / math.sqrt(D)
+    a = run_fused(q, k, v, theta, causal, scale)
+    b = run_rotated_k(q, k, v, theta, causal, scale)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert_parity(b, full_ref(q, k, v, theta, causal, scale), label="rotated-k %s" % ((B, Hq, Hkv, S, D, theta, causal),))
+
+
+def test_rope_pass_keys_only_equals_full_pass():
+    q, k, _ = make_qkv(2, 300, 4, 2, 128, seed=78)
+    qd, kd = _gpu(q, k)
+    _, kr_full = binding.attn_rope_apply(qd, kd, rope_theta=1e4)
+    q_none, kr_only = binding.attn_rope_apply(None, kd, rope_theta=1e4)
+    torch.cuda.synchronize()
+    assert q_none is None
+    assert torch.equal(kr_full.view(torch.int16), kr_only.view(torch.int16))
+
+
+@pytest.mark.parametrize("S,D,theta,kturns", [(700, 128, 5e5, 2.0), (300, 64, 1e4, 2.0)])
+def test_rotated_k_window_is_bitwise_fused(S, D, theta, kturns):
+    q, k, v = make_qkv(1, S, 4, 2, D, seed=3500 + S)
+    w = O.window_table(theta, D, kturns)
+    scale = 1 / math.sqrt(D)
+    a = run_fused(q, k, v, theta, True, scale, window=w)
+    b = run_rotated_k(q, k, v, theta, True, scale, window=w)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("name", ["prefill_s8192", "gqa_s16384"])
+def test_rotated_k_full_size_bitwise_fused(name):
+    cfg = CONFIGS[name]
+    B, Hq, Hkv, S, D, theta = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["S"], cfg["D"], cfg["theta"]
+    print("rotated-k full size %s" % name, flush=True)
+    q, k, v = make_qkv(B, S, Hq, Hkv, D, seed=CONFIG_SEEDS[name])
+    scale = 1 / math.sqrt(D)
+    qd, kd, vd = _gpu(q, k, v)
+    a = binding.attn_fwd(qd, kd, vd, rope_theta=theta, causal=True, scale=scale)
+    _, kr = binding.attn_rope_apply(None, kd, rope_theta=theta)
+    b = binding.attn_fwd_rotated_k(qd, kr, vd, rope_theta=theta, causal=True, scale=scale)
+    p = binding.attn_fwd_persistent(qd, kd, vd, rope_theta=theta, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert torch.equal(a.view(torch.int16), p.view(torch.int16))

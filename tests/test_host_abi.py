@@ -389,3 +389,20 @@ def test_decode_noalloc_limits_and_errors():
     assert _dec_noalloc_call(o=A) == binding.ATTN_EINVAL
     assert _dec_noalloc_call(scale=-1.0) == binding.ATTN_EINVAL
     assert _dec_noalloc_call(B=0) == binding.ATTN_OK
+
+
+def test_rope_apply_keys_only_argument_rules():
+    lib = binding.lib()
+    # q and q_out must both be NULL or both set
+    assert lib.attn_rope_apply(None, A, A * 64, A * 128, 1, 2, 2, 64, 128, 1e4, None) == binding.ATTN_EINVAL
+    assert lib.attn_rope_apply(A, A * 64, None, A * 128, 1, 2, 2, 64, 128, 1e4, None) == binding.ATTN_EINVAL
+    # keys only: the output must not overlap the input keys
+    assert lib.attn_rope_apply(None, A, None, A, 1, 2, 2, 64, 128, 1e4, None) == binding.ATTN_EINVAL
+    assert lib.attn_rope_apply(None, A, None, A * 64, 1, 2, 2, 64, 128, 0.0, None) == binding.ATTN_EINVAL
+
+
+def test_fwd_rotated_k_needs_theta():
+    """The query is rotated in the kernel: theta 0 is rejected before any
+    device call."""
+    st = binding.lib().attn_fwd_rotated_k(A, A * 64, A * 128, A * 192, 1, 2, 2, 64, 128, 0.0, 1, 0.088, None, None)
+    assert st == binding.ATTN_EINVAL
