@@ -311,3 +311,52 @@ def test_rotated_k_full_size_bitwise_fused(name):
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
     assert torch.equal(a.view(torch.int16), p.view(torch.int16))
+
+
+def test_window_all_pruned_gives_prefix_means():
+    """Every pair pruned at every distance (w_r = -1): every score is 0, so
+    causal row n is the mean of V over keys 0..n (closed form)."""
+    B, Hq, Hkv, S, D = 1, 4, 2, 700, 128
+    q, k, v = make_qkv(B, S, Hq, Hkv, D, seed=33)
+    w = np.full(D // 2, -1, dtype=np.int32)
+    o = run_fused(q, k, v, 1e4, True, 1 / math.sqrt(D), window=w).float().numpy().astype(np.float64)
+    vf = v.float().numpy().astype(np.float64)
+    ref = np.cumsum(vf, axis=1) / np.arange(1, S + 1)[None, :, None, None]
+    ref = np.repeat(ref, Hq // Hkv, axis=2)
+    err = np.abs(o - ref)
+    print("window all pruned max_abs=%.3e mean_abs=%.3e" % (err.max(), err.mean()), flush=True)
+    assert err.max() <= MAX_TOL and err.mean() <= MEAN_TOL
+
+
+def test_largest_supported_head_span_sampled():
+    """The largest size the 32-bit buffer offsets allow: one head's rows of Q
+    (and O) span S Hq D 2 bytes, just under 2^31 at S = 131071 (ragged),
+    Hq = 64, D = 128; the next S is rejected.  Inputs drawn on the GPU;
+    sampled rows of two heads (first and last, GQA 8:1) against the oracle,
+    which receives those heads only."""
+    B, Hq, Hkv, S, D, theta = 1, 64, 8, 131071, 128, 5e5
+    assert S * Hq * D * 2 < 2 ** 31 <= (S + 1) * Hq * D * 2
+    qd0 = torch.zeros(1, S + 1, Hq, D, dtype=torch.bfloat16, device="cuda:0")
+    with pytest.raises(binding.AttnError) as e:
+        binding.attn_fwd(qd0, qd0[:, :, :Hkv].contiguous(), qd0[:, :, :Hkv].contiguous())
+    assert e.value.status == binding.ATTN_EUNSUPPORTED
+    del qd0
+    print("largest head span: drawing inputs", flush=True)
+    g = torch.Generator(device="cuda:0").manual_seed(4242)
+    qd = torch.randn(B, S, Hq, D, device="cuda:0", generator=g, dtype=torch.float32).to(torch.bfloat16)
+    kd = torch.randn(B, S, Hkv, D, device="cuda:0", generator=g, dtype=torch.float32).to(torch.bfloat16)
+    vd = torch.randn(B, S, Hkv, D, device="cuda:0", generator=g, dtype=torch.float32).to(torch.bfloat16)
+    scale = 1 / math.sqrt(D)
+    o = binding.attn_fwd(qd, kd, vd, rope_theta=theta, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    heads = [0, Hq - 1]
+    q2 = qd[:, :, heads].cpu().contiguous()
+    k2 = kd[:, :, [h // (Hq // Hkv) for h in heads]].cpu().contiguous()
+    v2 = vd[:, :, [h // (Hq // Hkv) for h in heads]].cpu().contiguous()
+    o2 = o[:, :, heads].cpu()
+    rng = np.random.default_rng(7)
+    picks = [0, 1, 255, 256, 65535, S // 2, S - 257, S - 2, S - 1] + [int(x) for x in rng.integers(0, S, 5)]
+    rows = np.array([(0, n, h) for n in picks for h in (0, 1)], dtype=np.int32)
+    ref = O.attn_rows(bf16_bits(q2), bf16_bits(k2), bf16_bits(v2), rows, theta, True, scale, None)
+    assert_parity(o2, ref, rows=rows, label="largest head span S=%d" % S)
+    assert torch.isfinite(o.float()).all()
