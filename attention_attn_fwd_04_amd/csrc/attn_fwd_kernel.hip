@@ -108,12 +108,28 @@ struct Geo {
     // K (and cos/sin) tiles are stored as rows of ROWB bytes whose 16-byte
     // chunks are XOR-permuted per row: 16 lanes reading one logical chunk of
     // 16 consecutive rows hit 16 distinct 4-bank groups.
-    static __device__ __forceinline__ int kx(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
-    static __device__ __forceinline__ int k_off(int r, int c) { return r * ROWB + ((c ^ kx(r)) << 4); }
+    static constexpr __host__ __device__ int kx(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+    static constexpr __host__ __device__ int k_off(int r, int c) { return r * ROWB + ((c ^ kx(r)) << 4); }
     // V tiles: the 4 rows x 64 bytes half a wave of ds_read_b64_tr_b16 reads
     // land on distinct banks.
-    static __device__ __forceinline__ int vx(int r) { return D == 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2); }
-    static __device__ __forceinline__ int v_off(int r, int c) { return r * ROWB + ((c ^ vx(r)) << 4); }
+    static constexpr __host__ __device__ int vx(int r) { return D == 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2); }
+    static constexpr __host__ __device__ int v_off(int r, int c) { return r * ROWB + ((c ^ vx(r)) << 4); }
+    // The kernel forms the operand offsets of every chunk / block from one per
+    // lane by an XOR below bit 10, applied after adding a 1 KiB aligned slot
+    // base (which leaves those bits as they are): the identities hold for
+    // every row of a tile.
+    static constexpr bool offsets_by_xor() {
+        for (int r = 0; r < kBN; ++r)
+            for (int g = 0; g < 2; ++g) {
+                for (int kc = 0; kc < KCH; ++kc)
+                    if (k_off(r, kc + PG * g) != (k_off(r, PG * g) ^ (kc << 4)) || (kc << 4) >= 1024) return false;
+                for (int t = 0; t < 4; ++t)
+                    for (int db = 0; db < DB; ++db)
+                        if (v_off(r, 4 * db + t) != (v_off(r, t) ^ (db << 6)) || (db << 6) >= 1024) return false;
+            }
+        return TILE_B % 1024 == 0 && KSLOTS * TILE_B % 1024 == 0;
+    }
+    static_assert(offsets_by_xor(), "operand offsets by XOR from one base");
 };
 
 // PERSIST false: one work-group per query tile (work decoded from the block
@@ -127,7 +143,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
 {
     static_assert(ROPE || !ROPE_K, "keys are rotated in the kernel only with the query");
     using G = Geo<D, ROPE_K>;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[G::LDS_BYTES];
+    // (1 KiB aligned: so are the ring slots, whose bases then leave the low 10
+    // bits of an operand address, where the chunk XOR acts, unchanged)
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[G::LDS_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -305,19 +323,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
         // Per-lane LDS byte offsets of the MFMA operands within a tile.
         // K operand of k-step kc: row l32 (+32 for the second key block), logical
         // chunk kc + PG g.
-        int k_addr[G::KCH];
-#pragma unroll
-        for (int kc = 0; kc < G::KCH; ++kc) k_addr[kc] = G::k_off(l32, kc + G::PG * g);
+        // The chunk index enters k_off only through an XOR on bits disjoint from
+        // the row's, and kc < PG: k_off(l32, kc + PG g) == k_addr0 ^ (kc << 4).
+        // One base per lane instead of KCH offsets kept through the loop.
+        const int k_addr0 = G::k_off(l32, G::PG * g);
         // PV A operand through ds_read_b64_tr_b16: within each 16-lane group,
         // source lane s reads key (s / 4) of a 4-key group at dims D0 + 4 (s % 4)
         // .. +3, D0 = 32 db + 16 ((lane / 16) % 2); lane i of the group then holds
         // dim D0 + i of those 4 keys.  Key rows 16 ch + 4 g + s / 4 (+8).
         const int tr_key = (lane & 15) >> 2;
         const int tr_dim = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-        int v_addr[G::DB];
-#pragma unroll
-        for (int db = 0; db < G::DB; ++db)
-            v_addr[db] = G::v_off(4 * g + tr_key, (32 * db + tr_dim) >> 3) + 2 * (tr_dim & 4);
+        // Likewise v_off(r, 4 db + t) == v_off(r, t) ^ (db << 6) for t < 4:
+        // V operand offset of block db = v_addr0 ^ (db << 6).
+        const int v_addr0 = G::v_off(4 * g + tr_key, tr_dim >> 3) + 2 * (tr_dim & 4);
 
         // Causal / sequence-end mask of tile t, needed only on the tiles that
         // cross the wave's first row or the end of the sequence.
@@ -450,7 +468,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
             uint32_t kp[G::KCH];
 #pragma unroll
             for (int kc = 0; kc < G::KCH; ++kc) {
-                kp[kc] = kbase + (uint32_t)k_addr[kc];
+                kp[kc] = (kbase + (uint32_t)k_addr0) ^ (uint32_t)(kc << 4);
                 asm("" : "+v"(kp[kc]));
             }
             bf16x8_t kop[NM1];
@@ -527,7 +545,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
             uint32_t kp[G::KCH];
 #pragma unroll
             for (int kc = 0; kc < G::KCH; ++kc) {
-                kp[kc] = kbase + (uint32_t)k_addr[kc];
+                kp[kc] = (kbase + (uint32_t)k_addr0) ^ (uint32_t)(kc << 4);
                 asm("" : "+v"(kp[kc]));
             }
             bf16x8_t kop[NM];
@@ -597,7 +615,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
             uint32_t vp[G::DB];
 #pragma unroll
             for (int db = 0; db < G::DB; ++db) {
-                vp[db] = vbase + (uint32_t)v_addr[db];
+                vp[db] = (vbase + (uint32_t)v_addr0) ^ (uint32_t)(db << 6);
                 asm("" : "+v"(vp[db]));
             }
             i16x4_t vt0[NM2], vt1[NM2];
@@ -683,32 +701,39 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
         // S(i) into sc, with K(i+1) rotated alongside.
         // Block 1 with S(i); also issues the loads of iteration i.
         // With a window: the distances of this wave's 32 queries to the two
-        // 32-key blocks of tile i lie in [dlo, dhi] (dlo clamped at 0: causally
-        // masked cells are discarded later; dhi clipped to stored rows); the
-        // variant NS is the even number of leading chunks pruned on both blocks,
-        // valid if every chunk from NS + 2 on is kept on both (else the generic
-        // one).  VARIANTS false: the generic variant only.
-        auto scores_w = [&](auto variants_c, int i) __attribute__((always_inline)) {
-            uint64_t wprune[2], wkeep[2];
+        // 32-key blocks of tile t lie in [dlo, dhi] (dlo clamped at 0: causally
+        // masked cells are discarded later; dhi clipped to stored rows).
+        struct WinMasks { uint64_t prune[2], keep[2]; };
+        auto win_masks = [&](int t) __attribute__((always_inline)) {
+            WinMasks m;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                const int mk0 = i * kBN + kb * 32;
+                const int mk0 = t * kBN + kb * 32;
                 const int dlo = max(0, nw0 - (mk0 + 31)), dhi = min(nw0 + 31, S - 1) - mk0;
-                wprune[kb] = __builtin_amdgcn_ballot_w64(w_lane < dlo);
-                wkeep[kb] = ~__builtin_amdgcn_ballot_w64(w_lane < dhi);
+                m.prune[kb] = __builtin_amdgcn_ballot_w64(w_lane < dlo);
+                m.keep[kb] = ~__builtin_amdgcn_ballot_w64(w_lane < dhi);
             }
-            int ns = -1;
-            if constexpr (decltype(variants_c)::value) {
-                const uint64_t pr = wprune[0] & wprune[1], kp = wkeep[0] & wkeep[1];
-                const int lead = (~pr == 0) ? 64 : __builtin_ctzll(~pr);
-                ns = min((lead >> 3) & ~1, G::KCH - 2);
-                const int top = 8 * (ns + 2);
-                if (top < 64 && (kp | ((1ull << top) - 1)) != ~0ull) ns = -1;
-            }
+            return m;
+        };
+        // The variant NS of a tile: the even number of leading chunks pruned on
+        // both blocks, valid if every chunk from NS + 2 on is kept on both (else
+        // -1, the generic one).
+        auto win_variant = [&](const WinMasks &m) __attribute__((always_inline)) {
+            const uint64_t pr = m.prune[0] & m.prune[1], kp = m.keep[0] & m.keep[1];
+            const int lead = (~pr == 0) ? 64 : __builtin_ctzll(~pr);
+            int ns = min((lead >> 3) & ~1, G::KCH - 2);
+            const int top = 8 * (ns + 2);
+            if (top < 64 && (kp | ((1ull << top) - 1)) != ~0ull) ns = -1;
+            return ns;
+        };
+        // S(i) with a window: the variant chosen at run time, then the partial
+        // pairs.  VARIANTS false: the generic variant only.
+        auto scores_w = [&](auto variants_c, int i, const WinMasks &m) __attribute__((always_inline)) {
+            const int ns = decltype(variants_c)::value ? win_variant(m) : -1;
             const bool rot = rot_on(i);
             auto run = [&](auto ns_c) __attribute__((always_inline)) {
-                if (rot) block1w(std::true_type{}, ns_c, i, wprune, wkeep);
-                else block1w(std::false_type{}, ns_c, i, wprune, wkeep);
+                if (rot) block1w(std::true_type{}, ns_c, i, m.prune, m.keep);
+                else block1w(std::false_type{}, ns_c, i, m.prune, m.keep);
             };
             if constexpr (decltype(variants_c)::value) {
                 static_assert(G::KCH == 4 || G::KCH == 8, "variant list");
@@ -725,18 +750,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
             const uint32_t kbase = lds_addr(kslot(i));
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
-                if (const uint64_t part = ~(wprune[kb] | wkeep[kb]))
+                if (const uint64_t part = ~(m.prune[kb] | m.keep[kb]))
                     window_partial(sc[kb], part, kbase + (uint32_t)(kb * 32 * G::ROWB), i * kBN + kb * 32);
             if (need_mask(i)) mask_tile(sc, i);
         };
         auto scores = [&](int i) __attribute__((always_inline)) {
-            if constexpr (WINDOW) {
-                scores_w(std::true_type{}, i);
-            } else {
-                if (rot_on(i)) block1(std::true_type{}, i);
-                else block1(std::false_type{}, i);
-                if (need_mask(i)) mask_tile(sc, i);
-            }
+            if (rot_on(i)) block1(std::true_type{}, i);
+            else block1(std::false_type{}, i);
+            if (need_mask(i)) mask_tile(sc, i);
         };
         auto accept = [&](float rs, bf16x8_t (&pn)[kBN / 16]) __attribute__((always_inline)) {
             if (__builtin_amdgcn_ballot_w64(!(rs <= kLazyMaxSum)) != 0) rs = rescale_exp_tile(sc, pn);
@@ -745,6 +766,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
         // Steady state, 1 <= i < wave_tiles: S(i) || rotation; PV(i-1) from pp || P(i) into pn.
         auto steady = [&](int i, const bf16x8_t (&pp)[kBN / 16], bf16x8_t (&pn)[kBN / 16]) __attribute__((always_inline)) {
             scores(i);   // issues the loads of iteration i between its MFMAs
+            accept(block2(std::true_type{}, i, pp, pn), pn);
+            finish(i);
+        };
+        // The same with a window (the masks of tile i taken at its start).
+        auto steady_w = [&](int i, const bf16x8_t (&pp)[kBN / 16], bf16x8_t (&pn)[kBN / 16]) __attribute__((always_inline)) {
+            scores_w(std::true_type{}, i, win_masks(i));
             accept(block2(std::true_type{}, i, pp, pn), pn);
             finish(i);
         };
@@ -776,7 +803,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
         int i = 0;
         if (wave_tiles > 0) {
             // iteration 0: S(0), P(0) into pf_a
-            if constexpr (WINDOW) scores_w(std::false_type{}, 0);
+            if constexpr (WINDOW) scores_w(std::false_type{}, 0, win_masks(0));
             else scores(0);
             l_run = first_exp_tile(sc, pf_a);
             finish(0);
@@ -784,7 +811,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
                 // One iteration per trip (the window variants make the body
                 // large): P moves from pf_b back to pf_a.
                 for (i = 1; i < wave_tiles; ++i) {
-                    steady(i, pf_a, pf_b);
+                    steady_w(i, pf_a, pf_b);
 #pragma unroll
                     for (int ch = 0; ch < kBN / 16; ++ch) pf_a[ch] = pf_b[ch];
                 }

@@ -152,30 +152,27 @@ __device__ __forceinline__ bf16x8_t mask_pairs(bf16x8_t x, uint32_t keep_bits)
     return __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
 }
 
-// The same masks as a table in constant memory, for keep bits that are
-// wave-uniform: entry b holds the four operand-word masks of mask_pairs(., b),
-// fetched with one scalar load.
-struct alignas(16) PairMaskTable {
-    uint32_t w[256][4];
-};
-constexpr PairMaskTable make_pair_masks()
-{
-    PairMaskTable t{};
-    for (int b = 0; b < 256; ++b)
-        for (int i = 0; i < 4; ++i)
-            t.w[b][i] = (((b >> (2 * i)) & 1) ? 0x0000ffffu : 0u) | (((b >> (2 * i + 1)) & 1) ? 0xffff0000u : 0u);
-    return t;
-}
-__constant__ PairMaskTable kPairMasks = make_pair_masks();
-
 struct WordMask {
     uint32_t m[4];
 };
+// The same masks for keep bits that are wave-uniform, built in scalar
+// registers: s_bitreplicate_b64_b32 writes each bit of its 32-bit source
+// twice into a 64-bit result, so four rounds spread each of the 8 keep bits
+// over 16 bits, and word i of the result masks pairs 2i and 2i+1.  (No memory
+// access: a scalar load here would share its wait counter with the LDS operand
+// reads in flight, and its wait would drain them.)
+__device__ __forceinline__ uint64_t bit_replicate(uint32_t x)
+{
+    uint64_t r;
+    asm("s_bitreplicate_b64_b32 %0, %1" : "=s"(r) : "s"(x));
+    return r;
+}
 __device__ __forceinline__ WordMask pair_mask(uint64_t keep, int kc)
 {
     const uint32_t b = (uint32_t)(keep >> (8 * kc)) & 0xffu;
-    const uint4 t = *reinterpret_cast<const uint4 *>(&kPairMasks.w[b][0]);
-    return WordMask{{t.x, t.y, t.z, t.w}};
+    const uint64_t r3 = bit_replicate((uint32_t)bit_replicate((uint32_t)bit_replicate(b)));   // each bit x8
+    const uint64_t lo = bit_replicate((uint32_t)r3), hi = bit_replicate((uint32_t)(r3 >> 32));   // x16
+    return WordMask{{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)}};
 }
 __device__ __forceinline__ bf16x8_t apply_mask(bf16x8_t x, const WordMask &m)
 {
