@@ -445,6 +445,36 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
             }
         };
 
+        // ---- the softmax chain of one tile -------------------------------------
+        // Step e (0 .. 17): the exps of pair e (scores 2e, 2e+1 in P order:
+        // chunk e / 4, word e % 4; pairs 0-7 are key block 0), the bf16 packing
+        // of pair e-1, the fp32 row-sum adds of pair e-2, so that no instruction
+        // waits on the one just before it.  The steps are spread over MFMA
+        // segments of block 2, or of both blocks; the empty volatile asm
+        // statements pin each step before the next fence (without them the
+        // arithmetic is sunk below the last MFMA).
+        constexpr int NSTEP = 18;
+        float xr[4];
+        uint32_t xw[16];
+        float xpe[16][2];
+        auto exp_step = [&](int e) __attribute__((always_inline)) {
+            if (e < 16) {
+                const int ch = e >> 2, kb = ch >> 1, h = (ch & 1) * 8 + 2 * (e & 3);
+                xpe[e][0] = fast_exp2(sc[kb][h]);
+                xpe[e][1] = fast_exp2(sc[kb][h + 1]);
+                asm volatile("" : "+v"(xpe[e][0]), "+v"(xpe[e][1]));
+            }
+            if (e >= 1 && e <= 16) {
+                xw[e - 1] = pack_bf16x2(xpe[e - 1][0], xpe[e - 1][1]);
+                asm volatile("" : "+v"(xw[e - 1]));
+            }
+            if (e >= 2) {
+                xr[(e - 2) & 1] += xpe[e - 2][0];
+                xr[2 + ((e - 2) & 1)] += xpe[e - 2][1];
+                asm volatile("" : "+v"(xr[(e - 2) & 1]), "+v"(xr[2 + ((e - 2) & 1)]));
+            }
+        };
+
         // ---- the two steady-state blocks, hand-interleaved ---------------------
         // Each block is a sequence of segments, one per MFMA, fenced with
         // sched_barrier(0) so that the issue order is the one written here: the
@@ -459,8 +489,22 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
         // The unit's LDS reads go out after the first K operand reads (LDS
         // requests complete in order: issued first, they would hold up the
         // first MFMA) and are first used a few MFMAs later.
-        auto block1 = [&](auto rot_c, int i) __attribute__((always_inline)) {
+        // EXPS: the tile's scores need no mask, and the chain of key block 0
+        // runs first (after both chains' first MFMAs, so that the -m_ref seed
+        // is dead after two), finishing at MFMA KCH; the first E1 softmax steps,
+        // on block 0's scores, then go with MFMAs KCH + 2 .. 2 KCH - 1.  The
+        // sums are those of the alternating order (each chain adds its chunks
+        // in the same order), so the outputs do not depend on EXPS.
+        auto block1 = [&](auto rot_c, auto exps_c, int i) __attribute__((always_inline)) {
             constexpr bool ROT = decltype(rot_c)::value;
+            constexpr bool EXPS = decltype(exps_c)::value;
+            // MFMA k: key block kb_of(k), chunk kc_of(k)
+            auto kb_of = [&](int k) __attribute__((always_inline)) {
+                return EXPS ? (k == 1 || k > G::KCH ? 1 : 0) : (k & 1);
+            };
+            auto kc_of = [&](int k) __attribute__((always_inline)) {
+                return EXPS ? (k <= 1 ? 0 : k <= G::KCH ? k - 1 : k - G::KCH) : (k >> 1);
+            };
             f32x16_t minit;   // -m_ref: the start of both QK chains
 #pragma unroll
             for (int e = 0; e < 16; ++e) minit[e] = -m_ref;
@@ -473,8 +517,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
             }
             bf16x8_t kop[NM1];
             auto kread = [&](int k) __attribute__((always_inline)) {
-                kop[k] = *(const lds_bf16x8_t *)(lds_ptr(kp[k >> 1]) + (k & 1) * 32 * G::ROWB);
+                kop[k] = *(const lds_bf16x8_t *)(lds_ptr(kp[kc_of(k)]) + kb_of(k) * 32 * G::ROWB);
             };
+            if constexpr (EXPS) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) xr[q] = 0.f;
+            }
             uint4 rlo, rhi, rcq, rsq;
             uint8_t *rks = kslot(i + 1);
             const int o_lo = G::k_off(r_key, r_pg), o_hi = G::k_off(r_key, G::PG + r_pg);
@@ -497,11 +545,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
                     constexpr int EVERY_DMA = (NM1 - 2) / NDMA;
                     if (k % EVERY_DMA == 1 && k / EVERY_DMA < NDMA) dma_step(i, k / EVERY_DMA);
                 }
-                const int kc = k >> 1, kb = k & 1;
+                const int kc = kc_of(k), kb = kb_of(k);
                 if (kc == 0) {
                     sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[k], qreg[kc], minit, 0, 0, 0);
                 } else {
                     sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[k], qreg[kc], sc[kb], 0, 0, 0);
+                }
+                if constexpr (EXPS) {
+                    if (k >= G::KCH + 2) exp_step(k - (G::KCH + 2));
                 }
                 if constexpr (ROT) {
                     constexpr int R0 = NM1 / 4 + 1, RS = (NM1 - 1 - R0) / 3;   // words at R0 + RS r
@@ -606,11 +657,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
         };
 
         // Block 2: O^T += V(i-1)^T P(i-1)^T from pp; with EXP, P(i) = 2^(S(i) c
-        // - m_ref) into pn, two scores per step, 16 steps spread over the MFMAs.
-        // Returns the lane's partial row sum of P(i) (fp32, before rounding).
-        auto block2 = [&](auto exp_c, int i, const bf16x8_t (&pp)[kBN / 16], bf16x8_t (&pn)[kBN / 16])
+        // - m_ref) into pn: softmax steps E1 .. 17 spread over the MFMAs (E1 > 0:
+        // block 1 took the first ones).  Returns the lane's partial row sum of
+        // P(i) (fp32, before rounding).
+        auto block2 = [&](auto exp_c, auto e1_c, int i, const bf16x8_t (&pp)[kBN / 16], bf16x8_t (&pn)[kBN / 16])
             __attribute__((always_inline)) {
             constexpr bool EXP = decltype(exp_c)::value;
+            constexpr int E1 = decltype(e1_c)::value;
             const uint32_t vbase = lds_addr(vslot(i - 1));
             uint32_t vp[G::DB];
 #pragma unroll
@@ -625,32 +678,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
                 vt0[k] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)p0);
                 vt1[k] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(p0 + 8 * G::ROWB));
             };
-            float r[4] = {0.f, 0.f, 0.f, 0.f};
-            uint32_t w[16];
-            float pe[16][2];
-            // Step e (0 .. 17) of the softmax chain, software-pipelined so that no
-            // instruction waits on the one just before it: the exps of pair e
-            // (scores 2e, 2e+1 in P order: chunk e / 4, word e % 4), the bf16
-            // packing of pair e-1, the fp32 row-sum adds of pair e-2.  The empty
-            // volatile asm statements pin each step before the next fence
-            // (without them the arithmetic is sunk below the last MFMA).
-            auto exp_step = [&](int e) __attribute__((always_inline)) {
-                if (e < 16) {
-                    const int ch = e >> 2, kb = ch >> 1, h = (ch & 1) * 8 + 2 * (e & 3);
-                    pe[e][0] = fast_exp2(sc[kb][h]);
-                    pe[e][1] = fast_exp2(sc[kb][h + 1]);
-                    asm volatile("" : "+v"(pe[e][0]), "+v"(pe[e][1]));
-                }
-                if (e >= 1 && e <= 16) {
-                    w[e - 1] = pack_bf16x2(pe[e - 1][0], pe[e - 1][1]);
-                    asm volatile("" : "+v"(w[e - 1]));
-                }
-                if (e >= 2) {
-                    r[(e - 2) & 1] += pe[e - 2][0];
-                    r[2 + ((e - 2) & 1)] += pe[e - 2][1];
-                    asm volatile("" : "+v"(r[(e - 2) & 1]), "+v"(r[2 + ((e - 2) & 1)]));
-                }
-            };
+            if constexpr (EXP && E1 == 0) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) xr[q] = 0.f;
+            }
 #pragma unroll
             for (int k = 0; k < PF; ++k) vread(k);
             __builtin_amdgcn_sched_barrier(0);
@@ -661,7 +692,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
                 const uint2 u0 = __builtin_bit_cast(uint2, vt0[k]), u1 = __builtin_bit_cast(uint2, vt1[k]);
                 const bf16x8_t va = __builtin_bit_cast(bf16x8_t, make_uint4(u0.x, u0.y, u1.x, u1.y));
                 acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pp[ch], acc_o[db], 0, 0, 0);
-                if constexpr (EXP) {
+                if constexpr (EXP && E1 == 0) {
                     constexpr int PER = 16 / NM2;   // exp steps per MFMA; the last MFMA also drains the chain
 #pragma unroll
                     for (int q = 0; q < PER; ++q) exp_step(k * PER + q);
@@ -669,15 +700,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
                         exp_step(16);
                         exp_step(17);
                     }
+                } else if constexpr (EXP) {
+                    // steps E1 + [k n / NM2, (k + 1) n / NM2), n = NSTEP - E1
+                    constexpr int NREM = NSTEP - E1;
+#pragma unroll
+                    for (int e = E1 + k * NREM / NM2; e < E1 + (k + 1) * NREM / NM2; ++e) exp_step(e);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
             if constexpr (EXP) {
 #pragma unroll
                 for (int ch = 0; ch < kBN / 16; ++ch)
-                    pn[ch] = __builtin_bit_cast(bf16x8_t, make_uint4(w[4 * ch], w[4 * ch + 1], w[4 * ch + 2], w[4 * ch + 3]));
+                    pn[ch] = __builtin_bit_cast(bf16x8_t, make_uint4(xw[4 * ch], xw[4 * ch + 1], xw[4 * ch + 2], xw[4 * ch + 3]));
             }
-            return (r[0] + r[1]) + (r[2] + r[3]);
+            return (xr[0] + xr[1]) + (xr[2] + xr[3]);
         };
 
         // ---- iterations ---------------------------------------------------------
@@ -755,31 +791,42 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
             if (need_mask(i)) mask_tile(sc, i);
         };
         auto scores = [&](int i) __attribute__((always_inline)) {
-            if (rot_on(i)) block1(std::true_type{}, i);
-            else block1(std::false_type{}, i);
+            if (rot_on(i)) block1(std::true_type{}, std::false_type{}, i);
+            else block1(std::false_type{}, std::false_type{}, i);
             if (need_mask(i)) mask_tile(sc, i);
         };
         auto accept = [&](float rs, bf16x8_t (&pn)[kBN / 16]) __attribute__((always_inline)) {
             if (__builtin_amdgcn_ballot_w64(!(rs <= kLazyMaxSum)) != 0) rs = rescale_exp_tile(sc, pn);
             l_run += rs;
         };
+        using E0 = std::integral_constant<int, 0>;
         // Steady state, 1 <= i < wave_tiles: S(i) || rotation; PV(i-1) from pp || P(i) into pn.
         auto steady = [&](int i, const bf16x8_t (&pp)[kBN / 16], bf16x8_t (&pn)[kBN / 16]) __attribute__((always_inline)) {
             scores(i);   // issues the loads of iteration i between its MFMAs
-            accept(block2(std::true_type{}, i, pp, pn), pn);
+            accept(block2(std::true_type{}, E0{}, i, pp, pn), pn);
+            finish(i);
+        };
+        // The same for a tile that needs no mask, with the first softmax steps
+        // (key block 0) under the MFMAs of block 1: only a wave's last tile can
+        // need the causal or sequence-end mask (for t <= wave_tiles - 2, 64 t + 63
+        // <= nw0 and 64 t + 64 < S).
+        auto steady_split = [&](int i, const bf16x8_t (&pp)[kBN / 16], bf16x8_t (&pn)[kBN / 16]) __attribute__((always_inline)) {
+            if (rot_on(i)) block1(std::true_type{}, std::true_type{}, i);
+            else block1(std::false_type{}, std::true_type{}, i);
+            accept(block2(std::true_type{}, std::integral_constant<int, G::KCH - 2>{}, i, pp, pn), pn);
             finish(i);
         };
         // The same with a window (the masks of tile i taken at its start).
         auto steady_w = [&](int i, const bf16x8_t (&pp)[kBN / 16], bf16x8_t (&pn)[kBN / 16]) __attribute__((always_inline)) {
             scores_w(std::true_type{}, i, win_masks(i));
-            accept(block2(std::true_type{}, i, pp, pn), pn);
+            accept(block2(std::true_type{}, E0{}, i, pp, pn), pn);
             finish(i);
         };
         // i = wave_tiles: the last PV; later iterations only load and rotate.
         auto last_pv = [&](int i, const bf16x8_t (&pp)[kBN / 16], bf16x8_t (&scratch_pf)[kBN / 16]) __attribute__((always_inline)) {
             issue(i);
             if (rot_on(i)) rotate_k(i + 1);
-            block2(std::false_type{}, i, pp, scratch_pf);
+            block2(std::false_type{}, E0{}, i, pp, scratch_pf);
             finish(i);
         };
         auto idle = [&](int i) __attribute__((always_inline)) {
@@ -816,11 +863,32 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
                     for (int ch = 0; ch < kBN / 16; ++ch) pf_a[ch] = pf_b[ch];
                 }
                 last_pv(i, pf_a, pf_b);
-            } else {
-                // P(j) is in pf_a for even j, in pf_b for odd j.
+            } else if constexpr (ROPE_K) {
+                // P(j) is in pf_a for even j, in pf_b for odd j.  (Block 1
+                // carries the key rotation here: all the exps stay in block 2.)
                 for (i = 1; i + 1 < wave_tiles; i += 2) {
                     steady(i, pf_a, pf_b);
                     steady(i + 1, pf_b, pf_a);
+                }
+                if (i < wave_tiles) {
+                    steady(i, pf_a, pf_b);
+                    ++i;
+                    last_pv(i, pf_b, pf_a);
+                } else {
+                    last_pv(i, pf_a, pf_b);
+                }
+            } else {
+                // P(j) is in pf_a for even j, in pf_b for odd j; the last tile
+                // takes the masked path.
+                for (i = 1; i + 2 < wave_tiles; i += 2) {
+                    steady_split(i, pf_a, pf_b);
+                    steady_split(i + 1, pf_b, pf_a);
+                }
+                if (i + 1 < wave_tiles) {   // one more unmasked tile (once per wave: P copied back)
+                    steady_split(i, pf_a, pf_b);
+#pragma unroll
+                    for (int ch = 0; ch < kBN / 16; ++ch) pf_a[ch] = pf_b[ch];
+                    ++i;
                 }
                 if (i < wave_tiles) {
                     steady(i, pf_a, pf_b);
