@@ -298,36 +298,44 @@ __global__ __launch_bounds__(kDecWaves * 64, 1) void decode_split_kernel(const D
     if (g == 0) *reinterpret_cast<float2 *>(a.part_ml + pidx * 2) = make_float2(m_run, l_tot);
 }
 
-// Phase 2: merge the splits of one (b, hq) through their log-sum-exp.  One
-// 256-thread work-group per (b, hq): the block max M of the split maxima, the
-// weights 2^((m_s - M) c) of the splits (kept in LDS) and the weighted sum of
-// l; then thread (j, d) sums the weighted partial outputs of dimension d over
-// the splits s = j mod (256 / D), and the groups' sums are added.
+// Phase 2: merge the splits of one (b, hq) through their log-sum-exp: the
+// max M of the split maxima, the weights 2^((m_s - M) c) of the splits, the
+// weighted sums of l and of the partial outputs.
 constexpr int kCombThreads = 256;
+constexpr int kCombDims = 32;   // output dims per combine work-group
 
-__device__ __forceinline__ float block_reduce(float x, float *red, bool is_max)
+// Max or sum of x over the work-group: within each wave by lane shuffles,
+// then over the waves through LDS (one barrier).
+__device__ __forceinline__ float wg_reduce(float x, float *red, bool is_max)
 {
-    const int tid = threadIdx.x;
-    red[tid] = x;
-    __syncthreads();
 #pragma unroll
-    for (int h = kCombThreads / 2; h > 0; h >>= 1) {
-        if (tid < h) red[tid] = is_max ? fmaxf(red[tid], red[tid + h]) : red[tid] + red[tid + h];
-        __syncthreads();
+    for (int off = 32; off > 0; off >>= 1) {
+        const float y = __shfl_xor(x, off, 64);
+        x = is_max ? fmaxf(x, y) : x + y;
     }
-    const float r = red[0];
+    const int tid = threadIdx.x;
+    if ((tid & 63) == 0) red[tid >> 6] = x;
     __syncthreads();
+    float r = red[0];
+#pragma unroll
+    for (int w = 1; w < kCombThreads / 64; ++w) r = is_max ? fmaxf(r, red[w]) : r + red[w];
+    __syncthreads();   // red is reused by the next reduction
     return r;
 }
 
+// One work-group per (sequence, query head, 32-dim slice of the output): the
+// split weights 2^((m_s - M) c) and l = sum_s w_s l_s are formed in every
+// slice's work-group (a few KB of partials), then 8 groups of 32 threads
+// each sum a strided share of the splits for the slice's dims, all their
+// loads in flight at once.
 template <int D>
-__global__ __launch_bounds__(kCombThreads, 1) void decode_combine_kernel(const DecodeArgs a)
+__global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(const DecodeArgs a)
 {
-    constexpr int NG = kCombThreads / D;
-    __shared__ float red[kCombThreads];
+    constexpr int NG = kCombThreads / kCombDims;
+    __shared__ float red[kCombThreads / 64];
     __shared__ float wsh[kMaxDecodeSplits];
-    __shared__ float accs[NG][D];
-    const int bh = blockIdx.x, tid = threadIdx.x;
+    __shared__ float accs[NG][kCombDims];
+    const int bh = blockIdx.x, d0 = blockIdx.y * kCombDims, tid = threadIdx.x;
     const int ns = a.n_split;
     const float c = a.scale_log2e;
     const float *ml = a.part_ml + (size_t)bh * ns * 2;
@@ -335,7 +343,7 @@ __global__ __launch_bounds__(kCombThreads, 1) void decode_combine_kernel(const D
 
     float mloc = -__builtin_inff();
     for (int s = tid; s < ns; s += kCombThreads) mloc = fmaxf(mloc, ml[2 * s]);
-    const float M = block_reduce(mloc, red, true);
+    const float M = wg_reduce(mloc, red, true);
     float lloc = 0.f;
     for (int s = tid; s < ns; s += kCombThreads) {
         const float ms = ml[2 * s];
@@ -343,20 +351,26 @@ __global__ __launch_bounds__(kCombThreads, 1) void decode_combine_kernel(const D
         wsh[s] = w;
         lloc += w * ml[2 * s + 1];
     }
-    const float lsum = block_reduce(lloc, red, false);   // its barriers also publish wsh
+    const float lsum = wg_reduce(lloc, red, false);   // its barriers also publish wsh
 
-    const int j = tid / D, d = tid % D;
-    float acc = 0.f;
-#pragma unroll 4
-    for (int s = j; s < ns; s += NG) acc += wsh[s] * po[(size_t)s * D + d];
-    accs[j][d] = acc;
+    const int j = tid / kCombDims, d = tid % kCombDims;
+    const float *pd = po + d0 + d;
+    float acc0 = 0.f, acc1 = 0.f;
+    int s = j;
+#pragma unroll 8
+    for (; s + NG < ns; s += 2 * NG) {
+        acc0 += wsh[s] * pd[(size_t)s * D];
+        acc1 += wsh[s + NG] * pd[(size_t)(s + NG) * D];
+    }
+    if (s < ns) acc0 += wsh[s] * pd[(size_t)s * D];
+    accs[j][d] = acc0 + acc1;
     __syncthreads();
-    if (tid < D) {
+    if (tid < kCombDims) {
         float t = 0.f;
 #pragma unroll
         for (int g2 = 0; g2 < NG; ++g2) t += accs[g2][tid];
-        a.o[(size_t)bh * D + tid] = (uint16_t)(pack_bf16x2(t / lsum, 0.f) & 0xffffu);
-        if (a.lse != nullptr && tid == 0)
+        a.o[(size_t)bh * D + d0 + tid] = (uint16_t)(pack_bf16x2(t / lsum, 0.f) & 0xffffu);
+        if (a.lse != nullptr && tid == 0 && blockIdx.y == 0)
             a.lse[bh] = (M * c + __builtin_amdgcn_logf(lsum)) * 0.693147180559945309f;
     }
 }
@@ -377,7 +391,9 @@ hipError_t launch_d(const DecodeArgs &a, hipStream_t stream)
     if (rope) e = a.use_window ? launch_split<D, true, true>(a, stream) : launch_split<D, true, false>(a, stream);
     else e = a.use_window ? launch_split<D, false, true>(a, stream) : launch_split<D, false, false>(a, stream);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)(a.B * a.Hq)), dim3(kCombThreads), 0, stream, a);
+    static_assert(D % kCombDims == 0, "combine slices");
+    hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)(a.B * a.Hq), (unsigned)(D / kCombDims)), dim3(kCombThreads), 0,
+                       stream, a);
     return hipGetLastError();
 }
 
