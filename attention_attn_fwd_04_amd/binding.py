@@ -15,6 +15,9 @@ import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libattn_mi355x.so")
+# The debug twin built with every direct-to-LDS load waited for as it is
+# issued; its outputs must be bitwise the pipelined library's.
+SERIAL_LIB_PATH = os.path.join(_PKG, "libattn_mi355x_serial.so")
 
 ATTN_OK = 0
 ATTN_EINVAL = -1
@@ -40,15 +43,43 @@ class AttnError(RuntimeError):
         super().__init__("%s failed: %s (status %d)" % (what, strerror(status), status))
 
 
+_loaded = {}
+
+
 def lib():
     """Load the built library (raises if it has not been built)."""
     global _lib
-    if _lib is not None:
+    if _lib is None:
+        _lib = _load(LIB_PATH)
+    return _lib
+
+
+class use_library:
+    """Route the wrappers' calls to another build of the library (for
+    example SERIAL_LIB_PATH) inside a `with` block."""
+
+    def __init__(self, path):
+        self.path = path
+
+    def __enter__(self):
+        global _lib
+        self.saved = lib()
+        _lib = _load(self.path)
         return _lib
-    if not os.path.exists(LIB_PATH):
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self.saved
+        return False
+
+
+def _load(path):
+    if path in _loaded:
+        return _loaded[path]
+    if not os.path.exists(path):
         raise RuntimeError("HIP library %s is not built; run `python -m "
-                           "attention_attn_fwd_04_amd.build`" % LIB_PATH)
-    L = ctypes.CDLL(LIB_PATH)
+                           "attention_attn_fwd_04_amd.build`" % path)
+    L = ctypes.CDLL(path)
     vp, i, f, d = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_double
     i32p = ctypes.POINTER(ctypes.c_int32)
     L.attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, f, i, f, i32p, vp]
@@ -85,7 +116,7 @@ def lib():
     L.attn_strerror.restype = ctypes.c_char_p
     L.attn_release.argtypes = []
     L.attn_release.restype = None
-    _lib = L
+    _loaded[path] = L
     return L
 
 

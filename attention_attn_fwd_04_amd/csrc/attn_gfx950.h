@@ -79,6 +79,24 @@ __device__ __forceinline__ T &lds_at(uint8_t *base, int off) { return *reinterpr
 // needs 5 before a VMEM instruction reads it, an SALU write of M0 needs 1
 // before an LDS DMA.  With fewer, a load can take a descriptor word's
 // previous value, another buffer's base address, and read out of bounds.
+//
+// Debug build (ATTN_SERIAL_LOADS=1): every such load is waited for right
+// after it is issued, so no load is ever in flight while the kernel goes on.
+// The arithmetic and its order are unchanged: the outputs must be bitwise
+// those of the pipelined build.  A read of a slot whose load the pipelined
+// kernel had not waited for, or a load overwriting a slot another wave still
+// reads, would make them differ.
+// The wait is part of the same statement as the load, so nothing the
+// compiler schedules can fall between them.
+#ifndef ATTN_SERIAL_LOADS
+#define ATTN_SERIAL_LOADS 0
+#endif
+#if ATTN_SERIAL_LOADS
+#define ATTN_LDS_LOAD_TAIL "\n\ts_waitcnt vmcnt(0)"
+#else
+#define ATTN_LDS_LOAD_TAIL ""
+#endif
+
 // The same kind of buffer resource as four 32-bit words (base, stride 0,
 // size, flags), for the inline assembly below, which takes it as a scalar
 // operand.
@@ -106,7 +124,7 @@ __device__ __forceinline__ void dma16(u32x4_t r, uint32_t voff, const uint8_t *l
     rs.y = __builtin_amdgcn_readfirstlane(r.y);
     rs.z = __builtin_amdgcn_readfirstlane(r.z);
     rs.w = __builtin_amdgcn_readfirstlane(r.w);
-    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ATTN_LDS_LOAD_TAIL
                  :
                  : "v"(voff), "s"(rs), "{m0}"(m0)
                  : "memory");
@@ -122,7 +140,7 @@ __device__ __forceinline__ void dma16(u32x4_t r, uint32_t voff, uint32_t lds_bas
     rs.y = __builtin_amdgcn_readfirstlane(r.y);
     rs.z = __builtin_amdgcn_readfirstlane(r.z);
     rs.w = __builtin_amdgcn_readfirstlane(r.w);
-    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ATTN_LDS_LOAD_TAIL
                  :
                  : "v"(voff), "s"(rs), "{m0}"(m0)
                  : "memory");

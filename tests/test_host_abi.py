@@ -33,6 +33,15 @@ def test_library_exports_every_declared_symbol():
     assert set(binding.EXPORTED) == set(names)
 
 
+def test_serial_load_build_exports_the_same_symbols():
+    """The debug twin (every direct-to-LDS load waited for as it is issued),
+    which the GPU race check compares against, is built beside the library
+    and exports the same C ABI."""
+    lib = ctypes.CDLL(binding.SERIAL_LIB_PATH)
+    for n in _declared_functions():
+        assert hasattr(lib, n), n
+
+
 def test_strerror_covers_every_status():
     for st in range(0, -8, -1):
         msg = binding.strerror(st)
