@@ -42,6 +42,22 @@ def test_serial_load_build_exports_the_same_symbols():
         assert hasattr(lib, n), n
 
 
+def test_use_library_routes_calls_and_restores():
+    """binding.use_library switches the wrappers to another build inside the
+    block (host-only calls here) and back to the library afterwards."""
+    main = binding.lib()
+    with binding.use_library(binding.SERIAL_LIB_PATH) as serial:
+        assert binding.lib() is serial and serial is not main
+        assert binding.strerror(binding.ATTN_EINVAL) == main.attn_strerror(binding.ATTN_EINVAL).decode()
+    assert binding.lib() is main
+    try:
+        with binding.use_library(binding.SERIAL_LIB_PATH):
+            raise KeyError("inside")
+    except KeyError:
+        pass
+    assert binding.lib() is main
+
+
 def test_strerror_covers_every_status():
     for st in range(0, -8, -1):
         msg = binding.strerror(st)
