@@ -7,6 +7,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -20,6 +21,19 @@
 namespace {
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Fault injection for tests of the error path: with ATTN_INJECT_LAUNCH_ERROR=1
+// in the environment (read once per process), every entry point that would
+// launch a kernel returns ATTN_ELAUNCH at that point instead, after all its
+// checks and set-up, without launching anything.
+bool inject_launch_error()
+{
+    static const bool on = [] {
+        const char *e = std::getenv("ATTN_INJECT_LAUNCH_ERROR");
+        return e != nullptr && e[0] == '1' && e[1] == '\0';
+    }();
+    return on;
+}
 
 bool overlaps(const void *a, size_t na, const void *b, size_t nb)
 {
@@ -342,7 +356,8 @@ int fwd_common(const void *q, const void *k, const void *v, void *o, float *lse,
         st = get_schedule(dev, B, Hq, S, &a.sched, &a.sched_bins);
         if (st != ATTN_OK) return st;
     }
-    if (attn::launch_attn_fwd(a, static_cast<hipStream_t>(stream)) != hipSuccess) return ATTN_ELAUNCH;
+    if (inject_launch_error() || attn::launch_attn_fwd(a, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return ATTN_ELAUNCH;
     return ATTN_OK;
 }
 
@@ -554,7 +569,8 @@ int decode_common(const void *q, const void *k, const void *v, void *o, float *l
         rope_inv_freq(rope_theta, D, inv_freq);
         rope_row(inv_freq, D, L - 1, a.rope_row);
     }
-    if (attn::launch_decode(a, static_cast<hipStream_t>(stream)) != hipSuccess) return ATTN_ELAUNCH;
+    if (inject_launch_error() || attn::launch_decode(a, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return ATTN_ELAUNCH;
     return ATTN_OK;
 }
 
@@ -663,7 +679,8 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *o, const v
     } else {
         a.kop = a.k;
     }
-    if (attn::launch_attn_bwd(a, static_cast<hipStream_t>(stream)) != hipSuccess) return ATTN_ELAUNCH;
+    if (inject_launch_error() || attn::launch_attn_bwd(a, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return ATTN_ELAUNCH;
     return ATTN_OK;
 }
 
@@ -696,7 +713,8 @@ int attn_rope_apply(const void *q, const void *k, void *q_out, void *k_out, int 
     a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.S = S; a.D = D;
     st = get_table(dev, D, rope_theta, S, &a.rope_cs);
     if (st != ATTN_OK) return st;
-    if (attn::launch_rope_pass(a, static_cast<hipStream_t>(stream)) != hipSuccess) return ATTN_ELAUNCH;
+    if (inject_launch_error() || attn::launch_rope_pass(a, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return ATTN_ELAUNCH;
     return ATTN_OK;
 }
 

@@ -48,7 +48,9 @@ typedef enum {
     ATTN_EUNSUPPORTED = -2, /* valid but not built: D not in {64, 128} */
     ATTN_EALIGN = -3,       /* a tensor pointer is not 16-byte aligned (lse: 4-byte) */
     ATTN_ENOMEM = -4,       /* device allocation of the cos/sin table failed */
-    ATTN_ELAUNCH = -5,      /* the HIP runtime refused the launch or a copy */
+    ATTN_ELAUNCH = -5,      /* the HIP runtime refused the launch or a copy (also returned,
+                               without launching, when the environment of the process sets
+                               ATTN_INJECT_LAUNCH_ERROR=1: a test hook for the error path) */
     ATTN_ENODEVICE = -6,    /* no HIP device / the current device is not gfx950 */
     ATTN_ESCRATCH = -7      /* attn_decode_noalloc: the partials exceed the static scratch */
 } attn_status;
