@@ -491,8 +491,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdArgs a)
         // first MFMA) and are first used a few MFMAs later.
         // EXPS: the tile's scores need no mask, and the chain of key block 0
         // runs first (after both chains' first MFMAs, so that the -m_ref seed
-        // is dead after two), finishing at MFMA KCH; the first E1 softmax steps,
-        // on block 0's scores, then go with MFMAs KCH + 2 .. 2 KCH - 1.  The
+        // is dead after two), finishing at MFMA KCH; the first KCH - 2 softmax
+        // steps (block 2's E1), on block 0's scores, then go one each with MFMAs
+        // KCH + 2 .. 2 KCH - 1.  The
         // sums are those of the alternating order (each chain adds its chunks
         // in the same order), so the outputs do not depend on EXPS.
         auto block1 = [&](auto rot_c, auto exps_c, int i) __attribute__((always_inline)) {
