@@ -56,7 +56,9 @@ def lib():
 
 class use_library:
     """Route the wrappers' calls to another build of the library (for
-    example SERIAL_LIB_PATH) inside a `with` block."""
+    example SERIAL_LIB_PATH) inside a `with` block.  It swaps the module's
+    library handle, so it is for tests and single-threaded tools: calls made
+    from other threads meanwhile go to the same build."""
 
     def __init__(self, path):
         self.path = path
